@@ -1,0 +1,391 @@
+"""Benchmark of the MoE expert hot path on one MI355X.
+
+A step is one pass of the path over one batch of the skewed ~35B-A3B-shaped
+layer (T=8192 tokens, H=2048, E=256 experts, top-8, I=512, Zipf(1.2)-biased
+routing): moe_permute -> moe_grouped_gemm_swiglu -> moe_unpermute_combine ->
+moe_unpermute_grad (backward of the combine). Inputs are synthetic and
+resident in HBM before timing starts. `value` is tokens/s of that step.
+
+The same run also times every call at the other workloads (permute/combine
+at T=4096 H=2048 E=64 K=6; reorder + special-expert combine of the R=8 x 32
+receive buffer; the unpermute backward at T=16384 H=4096), each with a 1 GiB
+cache flush before every timed launch, and the CPU oracle on a bounded sample
+of the layer workload (`cpu_baseline`). One JSON line goes to stdout.
+
+    python bench.py [--steps K] [--warmup W] [--no-ops] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_DENSE_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+METRIC = "MoE layer tokens/s; permute/combine HBM GB/s; grouped-GEMM TFLOP/s"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--op-iters", type=int, default=20)
+    ap.add_argument("--no-ops", action="store_true", help="skip the per-workload op table")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=1536)
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------------------- helpers
+
+def dbf(a, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)) \
+        .view(torch.bfloat16).to(dev)
+
+
+def dt(a, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+class Flusher:
+    """Writes 1 GiB between timed launches so no input sits in the 256 MB
+    Infinity Cache or the L2s when a timed launch starts."""
+
+    def __init__(self, dev):
+        import torch
+        self.buf = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+
+    def __call__(self):
+        self.buf.fill_(1.0)
+
+
+def time_op(fn, iters, flush=None, warm=2):
+    """Median / min device time (us) of fn() bracketed by events on the current stream."""
+    import torch
+    for _ in range(warm):
+        fn()
+    times = []
+    for _ in range(iters):
+        if flush is not None:
+            flush()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b) * 1e3)
+    return float(np.median(times)), float(np.min(times))
+
+
+def op_entry(name, us_med, us_min, nbytes=None, flops=None):
+    e = {"op": name, "us_median": round(us_med, 2), "us_min": round(us_min, 2)}
+    if nbytes is not None:
+        gbs = nbytes / (us_med * 1e-6) / 1e9
+        e.update(algorithmic_bytes=int(nbytes), gbs=round(gbs, 1),
+                 hbm_frac=round(gbs / HBM_PEAK_GBS, 4))
+    if flops is not None:
+        tf = flops / (us_med * 1e-6) / 1e12
+        e.update(flops=int(flops), tflops=round(tf, 1),
+                 mfma_frac=round(tf / BF16_DENSE_PEAK_TFLOPS, 4))
+    return e
+
+
+# ----------------------------------------------------------------------------- algorithmic work
+
+def permute_bytes(T, K, H, N):
+    return T * K * 4 + T * H * 2 + N * H * 2 + 2 * T * K * 4 + 0
+
+
+def combine_bytes(T, K, H, N, extra_rows=0):
+    return N * H * 2 + 3 * T * K * 4 + T * H * 2 + extra_rows * H * 2
+
+
+def grad_bytes(T, K, H, N):
+    return T * H * 2 + 2 * N * H * 2 + 2 * T * K * 4 + T * K * 4
+
+
+def reorder_bytes(N, H):
+    return 2 * N * H * 2 + 2 * N * 4
+
+
+def gemm_flops(N, H, I):
+    return 6 * N * H * I
+
+
+# ----------------------------------------------------------------------------- the layer step
+
+def layer_setup(dev):
+    import torch
+    import moe_workloads as W
+    import unpermute_combine_moe_amd as moe
+
+    g = W.gen_c3()
+    c = g["cfg"]
+    T, H, E, K, I = c["T"], c["H"], c["E"], c["K"], c["I"]
+    S = T * K
+    d = dict(cfg=c, host=g)
+    d["x"] = dbf(g["x"], dev)
+    d["ids"] = dt(g["expert_ids"], dev)
+    d["probs"] = dt(g["probs"], dev)
+    d["wg"], d["wu"], d["wd"] = (dbf(g[k], dev) for k in ("w_gate", "w_up", "w_down"))
+    d["grad_out"] = dbf(W.normal_bf16(W.rng_for(3 * 1000 + 7), (T, H)), dev)
+    bf = torch.bfloat16
+    d["permuted"] = torch.empty((S, H), dtype=bf, device=dev)
+    d["sorted_slot"] = torch.empty(S, dtype=torch.int32, device=dev)
+    d["row_of_slot"] = torch.empty((T, K), dtype=torch.int32, device=dev)
+    d["counts"] = torch.empty(E, dtype=torch.int32, device=dev)
+    d["offsets"] = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    d["h"] = torch.empty((S, I), dtype=bf, device=dev)
+    d["y"] = torch.empty((S, H), dtype=bf, device=dev)
+    d["out"] = torch.empty((T, H), dtype=bf, device=dev)
+    d["d_perm"] = torch.empty((S, H), dtype=bf, device=dev)
+    d["d_probs"] = torch.empty((T, K), dtype=torch.float32, device=dev)
+    d["ws_p"] = moe.workspace(moe.moe_permute_workspace_size(T, K, E), dev)
+    d["ws_g"] = moe.workspace(moe.moe_grouped_gemm_swiglu_workspace_size(E, S, H, I), dev)
+    return d
+
+
+def step_calls(d):
+    import unpermute_combine_moe_amd as moe
+
+    c = d["cfg"]
+    T, H, E, K, I = c["T"], c["H"], c["E"], c["K"], c["I"]
+    S = T * K
+
+    def permute():
+        moe.moe_permute(d["x"], d["ids"], T, H, K, E, d["permuted"], d["sorted_slot"],
+                        d["row_of_slot"], d["counts"], d["offsets"], d["ws_p"])
+
+    def gemm():
+        moe.moe_grouped_gemm_swiglu(d["permuted"], d["offsets"], E, S, H, I, d["wg"], d["wu"],
+                                    d["wd"], d["h"], d["y"], d["ws_g"])
+
+    def combine():
+        moe.moe_unpermute_combine(d["y"], S, d["row_of_slot"], None, d["ids"], d["probs"], T, K, H,
+                                  E, None, None, d["out"])
+
+    def grad():
+        moe.moe_unpermute_grad(d["grad_out"], d["y"], S, d["row_of_slot"], d["probs"], T, K, H,
+                               d["d_perm"], d["d_probs"])
+
+    return permute, gemm, combine, grad
+
+
+def run_layer(args, dev):
+    import torch
+
+    d = layer_setup(dev)
+    permute, gemm, combine, grad = step_calls(d)
+    for _ in range(args.warmup):
+        permute(); gemm(); combine(); grad()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        e = ev[i]
+        e[0].record(); permute(); e[1].record(); gemm(); e[2].record(); combine(); e[3].record()
+        grad(); e[4].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    seg = np.array([[e[j].elapsed_time(e[j + 1]) * 1e3 for j in range(4)] for e in ev])  # us
+    n_rows = int(d["offsets"][-1].item())
+    return d, wall, seg, n_rows
+
+
+# ----------------------------------------------------------------------------- per-workload ops
+
+def run_ops(args, dev, flush):
+    import torch
+    import moe_workloads as W
+    import unpermute_combine_moe_amd as moe
+
+    ops = []
+    # permute / combine, T=4096 H=2048 E=64 K=6
+    g = W.gen_c2()
+    c = g["cfg"]
+    T, H, E, K = c["T"], c["H"], c["E"], c["K"]
+    x, ids, probs = dbf(g["x"], dev), dt(g["expert_ids"], dev), dt(g["probs"], dev)
+    p = moe.permute_alloc(x, ids, E)
+    ws = moe.workspace(moe.moe_permute_workspace_size(T, K, E), dev)
+    N = int(p["expert_offsets"][-1].item())
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    f_perm = lambda: moe.moe_permute(x, ids, T, H, K, E, p["permuted"], p["sorted_slot"],
+                                     p["row_of_slot"], p["expert_counts"], p["expert_offsets"], ws)
+    f_comb = lambda: moe.moe_unpermute_combine(p["permuted"], T * K, p["row_of_slot"], None, ids,
+                                               probs, T, K, H, E, None, None, out)
+    ops.append(dict(workload=c["name"], **op_entry("permute", *time_op(f_perm, args.op_iters, flush),
+                                                   nbytes=permute_bytes(T, K, H, N))))
+    ops.append(dict(workload=c["name"], **op_entry("unpermute_combine",
+                                                   *time_op(f_comb, args.op_iters, flush),
+                                                   nbytes=combine_bytes(T, K, H, N))))
+    del x, p, out
+    # reorder + combine with special experts, R=8 x E_local=32, N=32768, H=4096
+    g = W.gen_c4()
+    c = g["cfg"]
+    R, El, N, H, T, K = c["R"], c["E_local"], c["N"], c["H"], c["T"], c["K"]
+    xr, counts = dbf(g["x_rank_major"], dev), dt(g["counts"], dev)
+    r = moe.reorder_alloc(xr, counts, R, El)
+    wsr = moe.workspace(moe.moe_rank_to_expert_reorder_workspace_size(R, El), dev)
+    f_reo = lambda: moe.moe_rank_to_expert_reorder(xr, counts, R, El, N, H, r["y"], r["perm"],
+                                                   r["inv_perm"], r["tokens_per_expert"],
+                                                   r["expert_offsets"], wsr)
+    keep = [dbf(g["ori_x"], dev), dt(g["alpha1"], dev), dt(g["alpha2"], dev),
+            dbf(g["const_v"], dev)]
+    sp = moe.make_special(c["num_zero"], c["num_copy"], c["num_const"], keep[0], keep[1], keep[2],
+                          (1, 0, 0), keep[3])
+    shared = dbf(g["shared_x"], dev)
+    src, ids4, probs4 = dt(g["slot_src_row"], dev), dt(g["expert_ids"], dev), dt(g["probs"], dev)
+    out4 = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    f_comb4 = lambda: moe.moe_unpermute_combine(r["y"], N, src, r["inv_perm"], ids4, probs4, T, K,
+                                                H, El, sp, shared, out4)
+    ids_np = g["expert_ids"]
+    need_ori = int(np.any((ids_np >= El + c["num_zero"]) & (ids_np < El + 12), axis=1).sum())
+    n_routed = int((ids_np < El).sum())
+    ops.append(dict(workload=c["name"], **op_entry("rank_to_expert_reorder",
+                                                   *time_op(f_reo, args.op_iters, flush),
+                                                   nbytes=reorder_bytes(N, H))))
+    ops.append(dict(workload=c["name"], **op_entry(
+        "unpermute_combine_special", *time_op(f_comb4, args.op_iters, flush),
+        nbytes=n_routed * H * 2 + 4 * T * K * 4 + 2 * T * H * 2 + need_ori * H * 2 + N * 4)))
+    del xr, r, keep, shared, out4
+    # unpermute backward, T=16384 H=4096 E=128 K=8
+    g = W.gen_c5()
+    c = g["cfg"]
+    T, H, E, K = c["T"], c["H"], c["E"], c["K"]
+    ids5 = dt(g["expert_ids"], dev)
+    p5 = moe.permute_alloc(None, ids5, E, rows=False)
+    gout, perm5, probs5 = dbf(g["grad_out"], dev), dbf(g["permuted"], dev), dt(g["probs"], dev)
+    dperm = torch.empty_like(perm5)
+    dprobs = torch.empty((T, K), dtype=torch.float32, device=dev)
+    N = T * K
+    f_grad = lambda: moe.moe_unpermute_grad(gout, perm5, N, p5["row_of_slot"], probs5, T, K, H,
+                                            dperm, dprobs)
+    ops.append(dict(workload=c["name"], **op_entry("unpermute_grad",
+                                                   *time_op(f_grad, args.op_iters, flush),
+                                                   nbytes=grad_bytes(T, K, H, N))))
+    del gout, perm5, dperm
+    # device-to-device copy of 1 GiB for reference
+    a = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev)
+    b = torch.empty_like(a)
+    us, usmin = time_op(lambda: b.copy_(a), 10, None)
+    ops.append(dict(workload="d2d_copy_1GiB", **op_entry("torch_copy", us, usmin,
+                                                         nbytes=2 * a.numel() * 2)))
+    return ops
+
+
+# ----------------------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(d, n_tok):
+    """The CPU oracle timed on the first n_tok tokens of the layer workload:
+    permute -> fp64 SwiGLU FFN of their rows -> combine -> combine backward."""
+    import oracle
+
+    g = d["host"]
+    c = d["cfg"]
+    E = c["E"]
+    n_tok = min(n_tok, c["T"])
+    x, ids, probs = g["x"][:n_tok], g["expert_ids"][:n_tok], g["probs"][:n_tok]
+    import moe_workloads as W
+    gout = W.normal_bf16(W.rng_for(3 * 1000 + 7), (c["T"], c["H"]))[:n_tok]
+    t0 = time.perf_counter()
+    p = oracle.permute(x, ids, E)
+    _, y64 = oracle.grouped_swiglu(p["permuted"], p["expert_offsets"], g["w_gate"], g["w_up"],
+                                   g["w_down"], want_h=False)
+    y = oracle.f64_to_bf16(y64)
+    oracle.combine(y, p["row_of_slot"], ids, probs, E)
+    oracle.unpermute_grad(gout, y, p["row_of_slot"], probs)
+    el = time.perf_counter() - t0
+    return {"value": round(n_tok / el, 2), "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"first {n_tok} of {c['T']} tokens of the layer workload "
+                      f"({n_tok * c['K']} routed rows), same step: permute, fp64 SwiGLU FFN, "
+                      f"combine, combine backward; {el:.1f} s on {platform.processor() or 'host'}"}
+
+
+# ----------------------------------------------------------------------------- main
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this library has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import __graft_entry__ as ge
+    ge._ensure_built()
+    import unpermute_combine_moe_amd as moe
+    moe.load()
+    dev = torch.device("cuda:0")
+    log(f"device: {torch.cuda.get_device_name(0)}")
+
+    d, wall, seg, n_rows = run_layer(args, dev)
+    c = d["cfg"]
+    T, H, K, I = c["T"], c["H"], c["K"], c["I"]
+    ms_step = wall / args.steps * 1e3
+    seg_med = np.median(seg, axis=0)
+    log(f"layer step {ms_step:.3f} ms; permute {seg_med[0]:.1f} us, gemm {seg_med[1]:.1f} us, "
+        f"combine {seg_med[2]:.1f} us, grad {seg_med[3]:.1f} us")
+    g_us = float(np.mean(seg[:, 1]))
+    g_tf = gemm_flops(n_rows, H, I) / (g_us * 1e-6) / 1e12
+    roofline = {"bound": "mfma", "kernel": "moe_grouped_gemm_swiglu (sched + gate/up + down)",
+                "achieved": round(g_tf, 1), "peak": BF16_DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(g_tf / BF16_DENSE_PEAK_TFLOPS, 4), "traffic": None,
+                "avg_us": round(g_us, 2), "flops_per_launch": gemm_flops(n_rows, H, I)}
+    layer_ops = [
+        dict(workload=c["name"], **op_entry("permute", float(np.median(seg[:, 0])),
+                                            float(np.min(seg[:, 0])),
+                                            nbytes=permute_bytes(T, K, H, n_rows))),
+        dict(workload=c["name"], **op_entry("grouped_gemm_swiglu", float(np.median(seg[:, 1])),
+                                            float(np.min(seg[:, 1])),
+                                            flops=gemm_flops(n_rows, H, I))),
+        dict(workload=c["name"], **op_entry("unpermute_combine", float(np.median(seg[:, 2])),
+                                            float(np.min(seg[:, 2])),
+                                            nbytes=combine_bytes(T, K, H, n_rows))),
+        dict(workload=c["name"], **op_entry("unpermute_grad", float(np.median(seg[:, 3])),
+                                            float(np.min(seg[:, 3])),
+                                            nbytes=grad_bytes(T, K, H, n_rows))),
+    ]
+    ops = layer_ops
+    if not args.no_ops:
+        flush = Flusher(dev)
+        ops = ops + run_ops(args, dev, flush)
+        del flush
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        cpu = cpu_baseline(d, args.cpu_sample_tokens)
+    line = {
+        "metric": METRIC, "value": round(T / (ms_step * 1e-3), 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": c["name"], "T": T, "H": H, "E": c["E"], "K": K, "I": I,
+                   "routing": "Zipf(1.2)-biased softmax top-8, renormalised",
+                   "step": "permute + grouped SwiGLU GEMM + combine + combine backward",
+                   "parallelism": "single GPU"},
+        "roofline": roofline, "cpu_baseline": cpu, "ops": ops,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,60 @@
+"""Shared test utilities: host <-> device transfers of bf16 bit arrays and the
+tolerance rules of the parity tests."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import moe_workloads as W
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def to_dev_bf16(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)) \
+        .view(torch.bfloat16).to(dev())
+
+
+def to_dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev())
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def f64(bits_arr: np.ndarray) -> np.ndarray:
+    return W.f32_from_bf16(bits_arr).astype(np.float64)
+
+
+def assert_rel(got: np.ndarray, ref: np.ndarray, rel: float = 1e-2, what: str = ""):
+    """Elementwise |got - ref| <= rel*|ref| + rel*rms(ref), rms over the whole tensor
+    (the second term covers elements that are near zero)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    if ref.size == 0:
+        return
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    err = np.abs(got - ref)
+    bound = rel * np.abs(ref) + rel * rms
+    bad = err > bound
+    assert not bad.any(), (f"{what}: {int(bad.sum())} of {ref.size} elements outside the "
+                           f"{rel} relative bound; worst err {err.max():.3e} (rms {rms:.3e})")
+
+
+def gemm_tol(H: int) -> float:
+    """Max-abs bound of the grouped GEMM against the fp64 oracle: 2e-2 * sqrt(H) / 64."""
+    return 2e-2 * np.sqrt(H) / 64.0
+
+
+def ulp_diff(a_bits: np.ndarray, b_bits: np.ndarray) -> int:
+    """Largest distance in bf16 units in the last place (sign-magnitude ordering)."""
+    def key(b):
+        b = b.astype(np.int32)
+        return np.where(b & 0x8000, -(b & 0x7FFF), b)
+    if a_bits.size == 0:
+        return 0
+    return int(np.max(np.abs(key(a_bits) - key(b_bits))))

@@ -1,0 +1,205 @@
+"""Host-side checks of libmoeperm (no GPU needed): the library loads, exports
+every entry point include/libmoeperm.h declares, and every argument check
+returns its status before anything is enqueued.
+
+The argument checks are driven with fake, never-dereferenced pointers; they run
+only where no GPU is visible, so that a check that wrongly passed could not
+launch a kernel on such pointers."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+import __graft_entry__ as ge
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libmoeperm.h")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+no_gpu = pytest.mark.skipif(torch.cuda.is_available(),
+                            reason="fake-pointer argument checks run only without a GPU")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    ge._ensure_built()
+    from unpermute_combine_moe_amd import binding
+
+    return binding.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    from unpermute_combine_moe_amd import binding
+
+    names = _declared()
+    assert set(names) == set(binding.EXPORTS), names
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (\w+)$", out, flags=re.M))
+    for n in names:
+        assert n in exported, n
+        assert hasattr(lib, n)
+    # nothing else of ours leaks out of the library
+    assert {s for s in exported if s.startswith("moe_")} == set(names)
+
+
+def test_status_strings_and_version(lib):
+    from unpermute_combine_moe_amd import binding
+
+    assert binding.status_str(0) == "MOE_OK"
+    assert binding.status_str(3) == "MOE_ERR_WORKSPACE"
+    assert binding.status_str(99) == "MOE_ERR_UNKNOWN"
+    assert lib.moe_abi_version() == 1
+
+
+def test_workspace_sizes(lib):
+    from unpermute_combine_moe_amd import binding as b
+
+    assert b.moe_permute_workspace_size(8192, 8, 256) >= 4 * 256
+    assert b.moe_permute_workspace_size(0, 8, 256) > 0
+    assert b.moe_rank_to_expert_reorder_workspace_size(8, 32) >= 4 * 8 * 32 * 4
+    assert b.moe_grouped_gemm_swiglu_workspace_size(256, 65536, 2048, 512) >= 8 * 257
+    with pytest.raises(b.MoeError):
+        b.moe_permute_workspace_size(10, 17, 4)
+    with pytest.raises(b.MoeError):
+        b.moe_permute_workspace_size(10, 2, 1025)
+    with pytest.raises(b.MoeError):
+        b.moe_rank_to_expert_reorder_workspace_size(512, 256)
+    with pytest.raises(b.MoeError) as e:
+        b.moe_grouped_gemm_swiglu_workspace_size(8, 100, 96, 64)
+    assert e.value.status == UNSUPPORTED
+
+
+P = 0x10000        # fake 16-byte aligned device address, never dereferenced
+PM = P + 2         # misaligned
+
+
+def _permute(lib, x=P, ids=P, T=16, H=64, K=2, E=4, perm=P, ss=P, ros=P, cnt=P, off=P, ws=P,
+             wsb=1 << 20):
+    return lib.moe_permute(x, ids, T, H, K, E, perm, ss, ros, cnt, off, ws, wsb, None)
+
+
+@no_gpu
+def test_permute_checks(lib):
+    assert _permute(lib, T=-1) == INVALID
+    assert _permute(lib, K=0) == INVALID
+    assert _permute(lib, K=17) == INVALID
+    assert _permute(lib, E=0) == INVALID
+    assert _permute(lib, E=1025) == INVALID
+    assert _permute(lib, T=2**30, K=4) == INVALID       # T*K past int32
+    assert _permute(lib, H=12) == UNSUPPORTED
+    assert _permute(lib, H=0) == INVALID
+    assert _permute(lib, ids=None) == INVALID
+    assert _permute(lib, ros=PM) == INVALID
+    assert _permute(lib, x=P + 8) == INVALID            # rows need 16-byte alignment
+    assert _permute(lib, x=None) == INVALID             # rows requested without x
+    assert _permute(lib, cnt=None) == INVALID
+    assert _permute(lib, ws=None) == WORKSPACE
+    assert _permute(lib, wsb=4) == WORKSPACE
+
+
+def _reorder(lib, x=P, cnt=P, R=8, El=32, N=1000, H=64, y=P, perm=P, inv=P, tpe=P, off=P, ws=P,
+             wsb=1 << 20):
+    return lib.moe_rank_to_expert_reorder(x, cnt, R, El, N, H, y, perm, inv, tpe, off, ws, wsb,
+                                          None)
+
+
+@no_gpu
+def test_reorder_checks(lib):
+    assert _reorder(lib, R=0) == INVALID
+    assert _reorder(lib, El=0) == INVALID
+    assert _reorder(lib, R=300, El=300) == INVALID
+    assert _reorder(lib, N=-1) == INVALID
+    assert _reorder(lib, N=2**31) == INVALID
+    assert _reorder(lib, y=None) == INVALID             # x given without y
+    assert _reorder(lib, H=4) == UNSUPPORTED
+    assert _reorder(lib, cnt=None) == INVALID
+    assert _reorder(lib, perm=None) == INVALID
+    assert _reorder(lib, inv=PM) == INVALID
+    assert _reorder(lib, ws=None) == WORKSPACE
+    assert _reorder(lib, wsb=8) == WORKSPACE
+
+
+def _gemm(lib, x=P, off=P, E=8, N=1000, H=256, I=128, wg=P, wu=P, wd=P, h=P, y=P, ws=P,
+          wsb=1 << 20):
+    return lib.moe_grouped_gemm_swiglu(x, off, E, N, H, I, wg, wu, wd, h, y, ws, wsb, None)
+
+
+@no_gpu
+def test_gemm_checks(lib):
+    assert _gemm(lib, E=0) == INVALID
+    assert _gemm(lib, E=1025) == INVALID
+    assert _gemm(lib, N=-5) == INVALID
+    assert _gemm(lib, H=0) == INVALID
+    assert _gemm(lib, H=96) == UNSUPPORTED
+    assert _gemm(lib, I=100) == UNSUPPORTED
+    assert _gemm(lib, off=None) == INVALID
+    assert _gemm(lib, wd=P + 4) == INVALID
+    assert _gemm(lib, y=None) == INVALID
+    assert _gemm(lib, ws=None) == WORKSPACE
+    assert _gemm(lib, wsb=4) == WORKSPACE
+
+
+def _combine(lib, eo=P, N=100, ros=P, rmap=None, ids=P, probs=P, T=50, K=2, H=64, E=8, sp=None,
+             shared=None, out=P):
+    from unpermute_combine_moe_amd.binding import MoeSpecialExperts
+
+    spp = ctypes.byref(sp) if isinstance(sp, MoeSpecialExperts) else None
+    return lib.moe_unpermute_combine(eo, N, ros, rmap, ids, probs, T, K, H, E, spp, shared, out,
+                                     None)
+
+
+@no_gpu
+def test_combine_checks(lib):
+    from unpermute_combine_moe_amd.binding import MoeSpecialExperts as S
+
+    assert _combine(lib, T=-1) == INVALID
+    assert _combine(lib, K=17) == INVALID
+    assert _combine(lib, H=10) == UNSUPPORTED
+    assert _combine(lib, E=0) == INVALID
+    assert _combine(lib, N=-1) == INVALID
+    assert _combine(lib, eo=None) == INVALID
+    assert _combine(lib, out=P + 2) == INVALID
+    assert _combine(lib, rmap=PM) == INVALID
+    assert _combine(lib, shared=P + 8) == INVALID
+    # the combine_v2 page: ori_x is required by copy / const experts, alpha and v by const ones
+    assert _combine(lib, sp=S(0, 1, 0, None, None, None, 0, 0, 0, None)) == INVALID
+    assert _combine(lib, sp=S(0, 0, 1, P, None, P, 1, 0, 0, P)) == INVALID
+    assert _combine(lib, sp=S(0, 0, 1, P, P, P, 1, 0, 0, None)) == INVALID
+    assert _combine(lib, sp=S(-1, 0, 0, None, None, None, 0, 0, 0, None)) == INVALID
+    # moe_expert_num + zero + copy + const must stay below 2^31 - 1
+    assert _combine(lib, E=8, sp=S(2**31 - 10, 1, 1, P, P, P, 1, 0, 0, P)) == INVALID
+
+
+def _grad(lib, g=P, perm=P, N=100, ros=P, probs=P, T=50, K=2, H=64, dperm=P, dprobs=P):
+    return lib.moe_unpermute_grad(g, perm, N, ros, probs, T, K, H, dperm, dprobs, None)
+
+
+@no_gpu
+def test_grad_checks(lib):
+    assert _grad(lib, T=-3) == INVALID
+    assert _grad(lib, K=0) == INVALID
+    assert _grad(lib, H=6) == UNSUPPORTED
+    assert _grad(lib, N=-1) == INVALID
+    assert _grad(lib, g=None) == INVALID
+    assert _grad(lib, dperm=P + 8) == INVALID
+    assert _grad(lib, dprobs=None) == INVALID
+    assert _grad(lib, probs=PM) == INVALID
+
+
+def test_binding_rejects_wrong_tensors(lib):
+    from unpermute_combine_moe_amd import binding as b
+
+    with pytest.raises(TypeError):
+        b._ptr(torch.zeros(4, dtype=torch.float32), torch.int32, "ids")
+    with pytest.raises(ValueError):
+        b._ptr(torch.zeros(4, dtype=torch.int32), torch.int32, "ids")   # host tensor

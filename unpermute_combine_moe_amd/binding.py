@@ -1,0 +1,279 @@
+"""ctypes binding of libmoeperm (include/libmoeperm.h).
+
+Argument marshalling only: every function here checks that the torch tensors it
+is handed have the dtype / device / contiguity the C ABI expects, passes their
+device pointers and the current HIP stream, and turns a non-OK status into a
+MoeError. All computation happens in the HIP kernels of libmoeperm.so; if the
+library is missing this module raises instead of computing anything itself.
+
+Functions named like the C entry points take every output buffer explicitly;
+the ``*_alloc`` helpers allocate outputs and workspace with torch first.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoeperm.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(5)
+
+_vp = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_str(status)} ({status})")
+
+
+class MoeSpecialExperts(ctypes.Structure):
+    _fields_ = [
+        ("num_zero", _i32), ("num_copy", _i32), ("num_const", _i32),
+        ("ori_x", _vp), ("alpha1", _vp), ("alpha2", _vp),
+        ("alpha_stride_t", _i64), ("alpha_stride_c", _i64), ("alpha_stride_h", _i64),
+        ("const_v", _vp),
+    ]
+
+
+EXPORTS = (
+    "moe_status_str", "moe_abi_version",
+    "moe_permute_workspace_size", "moe_permute",
+    "moe_rank_to_expert_reorder_workspace_size", "moe_rank_to_expert_reorder",
+    "moe_grouped_gemm_swiglu_workspace_size", "moe_grouped_gemm_swiglu",
+    "moe_unpermute_combine", "moe_unpermute_grad",
+)
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libmoeperm.so and declare its signatures. Raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"libmoeperm is not built ({path} missing); run "
+                          "`python -c 'import __graft_entry__ as g; g.build()'` first")
+    lib = ctypes.CDLL(path)
+    lib.moe_status_str.argtypes = [ctypes.c_int]
+    lib.moe_status_str.restype = ctypes.c_char_p
+    lib.moe_abi_version.argtypes = []
+    lib.moe_abi_version.restype = _i32
+    sz = ctypes.POINTER(ctypes.c_size_t)
+    lib.moe_permute_workspace_size.argtypes = [_i64, _i32, _i32, sz]
+    lib.moe_permute.argtypes = [_vp, _vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
+                                ctypes.c_size_t, _vp]
+    lib.moe_rank_to_expert_reorder_workspace_size.argtypes = [_i32, _i32, sz]
+    lib.moe_rank_to_expert_reorder.argtypes = [_vp, _vp, _i32, _i32, _i64, _i32, _vp, _vp, _vp,
+                                               _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    lib.moe_grouped_gemm_swiglu_workspace_size.argtypes = [_i32, _i64, _i32, _i32, sz]
+    lib.moe_grouped_gemm_swiglu.argtypes = [_vp, _vp, _i32, _i64, _i32, _i32, _vp, _vp, _vp, _vp,
+                                            _vp, _vp, ctypes.c_size_t, _vp]
+    lib.moe_unpermute_combine.argtypes = [_vp, _i64, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32,
+                                          ctypes.POINTER(MoeSpecialExperts), _vp, _vp, _vp]
+    lib.moe_unpermute_grad.argtypes = [_vp, _vp, _i64, _vp, _vp, _i64, _i32, _i32, _vp, _vp, _vp]
+    for name in EXPORTS[2:]:
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load().moe_status_str(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != MOE_OK:
+        raise MoeError(status, where)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t, dtype=None, name="tensor"):
+    """Device pointer of a contiguous tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.numel() > 0 and not t.is_cuda:
+        raise ValueError(f"{name}: expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tensor")
+    return t.data_ptr() if t.numel() > 0 else None
+
+
+_BF16 = torch.bfloat16
+_I32 = torch.int32
+_F32 = torch.float32
+
+
+# --------------------------------------------------------------------------- workspaces
+
+def moe_permute_workspace_size(T: int, K: int, E: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().moe_permute_workspace_size(T, K, E, ctypes.byref(n)), "moe_permute_workspace_size")
+    return n.value
+
+
+def moe_rank_to_expert_reorder_workspace_size(R: int, E_local: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().moe_rank_to_expert_reorder_workspace_size(R, E_local, ctypes.byref(n)),
+           "moe_rank_to_expert_reorder_workspace_size")
+    return n.value
+
+
+def moe_grouped_gemm_swiglu_workspace_size(E: int, N_cap: int, H: int, I: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().moe_grouped_gemm_swiglu_workspace_size(E, N_cap, H, I, ctypes.byref(n)),
+           "moe_grouped_gemm_swiglu_workspace_size")
+    return n.value
+
+
+def workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
+# --------------------------------------------------------------------------- calls
+
+def moe_permute(x, expert_ids, T, H, K, num_experts, permuted, sorted_slot, row_of_slot,
+                expert_counts, expert_offsets, ws, stream=None):
+    _check(load().moe_permute(
+        _ptr(x, _BF16, "x"), _ptr(expert_ids, _I32, "expert_ids"), T, H, K, num_experts,
+        _ptr(permuted, _BF16, "permuted"), _ptr(sorted_slot, _I32, "sorted_slot"),
+        _ptr(row_of_slot, _I32, "row_of_slot"), _ptr(expert_counts, _I32, "expert_counts"),
+        _ptr(expert_offsets, _I32, "expert_offsets"), _ptr(ws, None, "workspace"),
+        ws.numel() if ws is not None else 0, _stream(stream)), "moe_permute")
+
+
+def moe_rank_to_expert_reorder(x_rank_major, counts, R, E_local, N, H, y_expert_major, perm,
+                               inv_perm, tokens_per_expert, expert_offsets, ws, stream=None):
+    _check(load().moe_rank_to_expert_reorder(
+        _ptr(x_rank_major, _BF16, "x_rank_major"), _ptr(counts, _I32, "counts"), R, E_local, N, H,
+        _ptr(y_expert_major, _BF16, "y_expert_major"), _ptr(perm, _I32, "perm"),
+        _ptr(inv_perm, _I32, "inv_perm"), _ptr(tokens_per_expert, _I32, "tokens_per_expert"),
+        _ptr(expert_offsets, _I32, "expert_offsets"), _ptr(ws, None, "workspace"),
+        ws.numel() if ws is not None else 0, _stream(stream)), "moe_rank_to_expert_reorder")
+
+
+def moe_grouped_gemm_swiglu(x, expert_offsets, E, N_cap, H, I, w_gate, w_up, w_down, h, y, ws,
+                            stream=None):
+    _check(load().moe_grouped_gemm_swiglu(
+        _ptr(x, _BF16, "x"), _ptr(expert_offsets, _I32, "expert_offsets"), E, N_cap, H, I,
+        _ptr(w_gate, _BF16, "w_gate"), _ptr(w_up, _BF16, "w_up"), _ptr(w_down, _BF16, "w_down"),
+        _ptr(h, _BF16, "h"), _ptr(y, _BF16, "y"), _ptr(ws, None, "workspace"),
+        ws.numel() if ws is not None else 0, _stream(stream)), "moe_grouped_gemm_swiglu")
+
+
+def make_special(num_zero=0, num_copy=0, num_const=0, ori_x=None, alpha1=None, alpha2=None,
+                 alpha_strides=(0, 0, 0), const_v=None):
+    """Build the moe_special_experts_t struct; keep the tensors alive meanwhile."""
+    st, sc, sh = (int(v) for v in alpha_strides)
+    return MoeSpecialExperts(num_zero, num_copy, num_const, _ptr(ori_x, _BF16, "ori_x"),
+                             _ptr(alpha1, _F32, "alpha1"), _ptr(alpha2, _F32, "alpha2"), st, sc,
+                             sh, _ptr(const_v, _BF16, "const_v"))
+
+
+def moe_unpermute_combine(expert_out, N, row_of_slot, row_map, expert_ids, probs, T, K, H,
+                          num_experts, special, shared_x, out, stream=None):
+    sp = ctypes.byref(special) if special is not None else None
+    _check(load().moe_unpermute_combine(
+        _ptr(expert_out, _BF16, "expert_out"), N, _ptr(row_of_slot, _I32, "row_of_slot"),
+        _ptr(row_map, _I32, "row_map"), _ptr(expert_ids, _I32, "expert_ids"),
+        _ptr(probs, _F32, "probs"), T, K, H, num_experts, sp, _ptr(shared_x, _BF16, "shared_x"),
+        _ptr(out, _BF16, "out"), _stream(stream)), "moe_unpermute_combine")
+
+
+def moe_unpermute_grad(grad_out, permuted, N, row_of_slot, probs, T, K, H, d_permuted, d_probs,
+                       stream=None):
+    _check(load().moe_unpermute_grad(
+        _ptr(grad_out, _BF16, "grad_out"), _ptr(permuted, _BF16, "permuted"), N,
+        _ptr(row_of_slot, _I32, "row_of_slot"), _ptr(probs, _F32, "probs"), T, K, H,
+        _ptr(d_permuted, _BF16, "d_permuted"), _ptr(d_probs, _F32, "d_probs"), _stream(stream)),
+        "moe_unpermute_grad")
+
+
+# --------------------------------------------------------------------------- allocating helpers
+
+def permute_alloc(x, expert_ids, num_experts, *, rows: bool = True, stream=None):
+    T, K = expert_ids.shape
+    dev = expert_ids.device
+    H = x.shape[1] if rows else 0
+    S = T * K
+    out = dict(
+        permuted=torch.empty((S, H), dtype=_BF16, device=dev) if rows else None,
+        sorted_slot=torch.empty(S, dtype=_I32, device=dev),
+        row_of_slot=torch.empty((T, K), dtype=_I32, device=dev),
+        expert_counts=torch.empty(num_experts, dtype=_I32, device=dev),
+        expert_offsets=torch.empty(num_experts + 1, dtype=_I32, device=dev),
+    )
+    ws = workspace(moe_permute_workspace_size(T, K, num_experts), dev)
+    moe_permute(x if rows else None, expert_ids, T, H, K, num_experts, out["permuted"],
+                out["sorted_slot"], out["row_of_slot"], out["expert_counts"],
+                out["expert_offsets"], ws, stream)
+    return out
+
+
+def reorder_alloc(x_rank_major, counts, R, E_local, N=None, *, rows: bool = True, stream=None):
+    dev = counts.device
+    if N is None:
+        N = x_rank_major.shape[0]
+    H = x_rank_major.shape[1] if rows else 0
+    out = dict(
+        y=torch.empty((N, H), dtype=_BF16, device=dev) if rows else None,
+        perm=torch.empty(N, dtype=_I32, device=dev),
+        inv_perm=torch.empty(N, dtype=_I32, device=dev),
+        tokens_per_expert=torch.empty(E_local, dtype=_I32, device=dev),
+        expert_offsets=torch.empty(E_local + 1, dtype=_I32, device=dev),
+    )
+    ws = workspace(moe_rank_to_expert_reorder_workspace_size(R, E_local), dev)
+    moe_rank_to_expert_reorder(x_rank_major if rows else None, counts, R, E_local, N, H, out["y"],
+                               out["perm"], out["inv_perm"], out["tokens_per_expert"],
+                               out["expert_offsets"], ws, stream)
+    return out
+
+
+def grouped_gemm_alloc(x, expert_offsets, w_gate, w_up, w_down, *, stream=None):
+    E, H, I = w_gate.shape
+    N_cap = x.shape[0]
+    dev = x.device
+    h = torch.empty((N_cap, I), dtype=_BF16, device=dev)
+    y = torch.empty((N_cap, H), dtype=_BF16, device=dev)
+    ws = workspace(moe_grouped_gemm_swiglu_workspace_size(E, N_cap, H, I), dev)
+    moe_grouped_gemm_swiglu(x, expert_offsets, E, N_cap, H, I, w_gate, w_up, w_down, h, y, ws,
+                            stream)
+    return h, y
+
+
+def combine_alloc(expert_out, row_of_slot, expert_ids, probs, num_experts, *, row_map=None,
+                  special=None, shared_x=None, H=None, stream=None):
+    T, K = expert_ids.shape
+    if H is None:
+        H = expert_out.shape[1]
+    N = expert_out.shape[0] if expert_out is not None else 0
+    out = torch.empty((T, H), dtype=_BF16, device=expert_ids.device)
+    moe_unpermute_combine(expert_out, N, row_of_slot, row_map, expert_ids, probs, T, K, H,
+                          num_experts, special, shared_x, out, stream)
+    return out
+
+
+def unpermute_grad_alloc(grad_out, permuted, row_of_slot, probs, *, d_permuted=None, stream=None):
+    T, K = probs.shape
+    N, H = permuted.shape
+    if d_permuted is None:
+        d_permuted = torch.zeros((N, H), dtype=_BF16, device=permuted.device)
+    d_probs = torch.empty((T, K), dtype=_F32, device=permuted.device)
+    moe_unpermute_grad(grad_out, permuted, N, row_of_slot, probs, T, K, H, d_permuted, d_probs,
+                       stream)
+    return d_permuted, d_probs

@@ -1,0 +1,227 @@
+// C ABI of libmoeperm: host-side argument checks, then the launchers.
+// Every check runs before anything is enqueued; see include/libmoeperm.h for
+// the contract of each call.
+#include "libmoeperm.h"
+
+#include <limits.h>
+
+#include "launch.hpp"
+
+#define MOE_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int32_t kAbiVersion = 1;
+
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+// a row tensor: non-null and 16-byte aligned
+inline bool row_ok(const void* p) { return p != nullptr && aligned(p, 16); }
+// an int32 / fp32 tensor: non-null and 4-byte aligned
+inline bool word_ok(const void* p) { return p != nullptr && aligned(p, 4); }
+
+inline moe_status_t hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+const uint16_t* u16(const void* p) { return static_cast<const uint16_t*>(p); }
+uint16_t* u16(void* p) { return static_cast<uint16_t*>(p); }
+
+moe_status_t check_tk(int64_t T, int32_t K) {
+  if (T < 0 || K < 1 || K > MOE_MAX_TOPK) return MOE_ERR_INVALID_ARG;
+  if (T * int64_t(K) > INT32_MAX) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+moe_status_t check_h(int32_t H) {
+  if (H <= 0) return MOE_ERR_INVALID_ARG;
+  if (H % 8 != 0) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+}  // namespace
+
+MOE_API const char* moe_status_str(moe_status_t s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+MOE_API int32_t moe_abi_version(void) { return kAbiVersion; }
+
+// --------------------------------------------------------------------------- permute
+
+MOE_API moe_status_t moe_permute_workspace_size(int64_t T, int32_t K, int32_t E, size_t* bytes) {
+  if (bytes == nullptr) return MOE_ERR_INVALID_ARG;
+  if (moe_status_t s = check_tk(T, K)) return s;
+  if (E < 1 || E > MOE_MAX_EXPERTS) return MOE_ERR_INVALID_ARG;
+  *bytes = moe::permute_workspace_bytes(T, K, E);
+  return MOE_OK;
+}
+
+MOE_API moe_status_t moe_permute(const void* x, const int32_t* expert_ids, int64_t T, int32_t H,
+                                 int32_t K, int32_t num_experts, void* permuted,
+                                 int32_t* sorted_slot, int32_t* row_of_slot,
+                                 int32_t* expert_counts, int32_t* expert_offsets, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  if (moe_status_t s = check_tk(T, K)) return s;
+  if (num_experts < 1 || num_experts > MOE_MAX_EXPERTS) return MOE_ERR_INVALID_ARG;
+  if (permuted != nullptr) {
+    if (moe_status_t s = check_h(H)) return s;
+  }
+  if (!word_ok(expert_counts) || !word_ok(expert_offsets)) return MOE_ERR_INVALID_ARG;
+  if (T > 0) {
+    if (!word_ok(expert_ids) || !word_ok(sorted_slot) || !word_ok(row_of_slot))
+      return MOE_ERR_INVALID_ARG;
+    if (permuted != nullptr && (!row_ok(x) || !row_ok(permuted))) return MOE_ERR_INVALID_ARG;
+  }
+  const size_t need = moe::permute_workspace_bytes(T, K, num_experts);
+  if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 4))
+    return MOE_ERR_WORKSPACE;
+  return hip_status(moe::launch_permute(u16(x), expert_ids, T, H, K, num_experts, u16(permuted),
+                                        sorted_slot, row_of_slot, expert_counts, expert_offsets,
+                                        workspace, stream));
+}
+
+// --------------------------------------------------------------------------- reorder
+
+MOE_API moe_status_t moe_rank_to_expert_reorder_workspace_size(int32_t R, int32_t E_local,
+                                                               size_t* bytes) {
+  if (bytes == nullptr || R < 1 || E_local < 1 ||
+      int64_t(R) * E_local > MOE_MAX_REORDER_BLOCKS)
+    return MOE_ERR_INVALID_ARG;
+  *bytes = moe::reorder_workspace_bytes(R, E_local);
+  return MOE_OK;
+}
+
+MOE_API moe_status_t moe_rank_to_expert_reorder(const void* x_rank_major, const int32_t* counts,
+                                                int32_t R, int32_t E_local, int64_t N, int32_t H,
+                                                void* y_expert_major, int32_t* perm,
+                                                int32_t* inv_perm, int32_t* tokens_per_expert,
+                                                int32_t* expert_offsets, void* workspace,
+                                                size_t workspace_bytes, hipStream_t stream) {
+  if (R < 1 || E_local < 1 || int64_t(R) * E_local > MOE_MAX_REORDER_BLOCKS)
+    return MOE_ERR_INVALID_ARG;
+  if (N < 0 || N > INT32_MAX) return MOE_ERR_INVALID_ARG;
+  if ((x_rank_major == nullptr) != (y_expert_major == nullptr)) return MOE_ERR_INVALID_ARG;
+  if (y_expert_major != nullptr) {
+    if (moe_status_t s = check_h(H)) return s;
+    if (N > 0 && (!row_ok(x_rank_major) || !row_ok(y_expert_major))) return MOE_ERR_INVALID_ARG;
+  }
+  if (!word_ok(counts) || !word_ok(tokens_per_expert) || !word_ok(expert_offsets))
+    return MOE_ERR_INVALID_ARG;
+  if (N > 0 && !word_ok(perm)) return MOE_ERR_INVALID_ARG;
+  if (inv_perm != nullptr && !aligned(inv_perm, 4)) return MOE_ERR_INVALID_ARG;
+  const size_t need = moe::reorder_workspace_bytes(R, E_local);
+  if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 4))
+    return MOE_ERR_WORKSPACE;
+  return hip_status(moe::launch_reorder(u16(x_rank_major), counts, R, E_local, N, H,
+                                        u16(y_expert_major), perm, inv_perm, tokens_per_expert,
+                                        expert_offsets, workspace, stream));
+}
+
+// --------------------------------------------------------------------------- grouped GEMM
+
+namespace {
+moe_status_t check_gemm_sizes(int32_t E, int64_t N_cap, int32_t H, int32_t I) {
+  if (E < 1 || E > MOE_MAX_EXPERTS) return MOE_ERR_INVALID_ARG;
+  if (N_cap < 0 || N_cap > INT32_MAX) return MOE_ERR_INVALID_ARG;
+  if (H <= 0 || I <= 0) return MOE_ERR_INVALID_ARG;
+  if (H % 64 != 0 || I % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+}  // namespace
+
+MOE_API moe_status_t moe_grouped_gemm_swiglu_workspace_size(int32_t E, int64_t N_cap, int32_t H,
+                                                            int32_t I, size_t* bytes) {
+  if (bytes == nullptr) return MOE_ERR_INVALID_ARG;
+  if (moe_status_t s = check_gemm_sizes(E, N_cap, H, I)) return s;
+  *bytes = moe::gemm_workspace_bytes(E, N_cap, H, I);
+  return MOE_OK;
+}
+
+MOE_API moe_status_t moe_grouped_gemm_swiglu(const void* x, const int32_t* expert_offsets,
+                                             int32_t E, int64_t N_cap, int32_t H, int32_t I,
+                                             const void* w_gate, const void* w_up,
+                                             const void* w_down, void* h, void* y,
+                                             void* workspace, size_t workspace_bytes,
+                                             hipStream_t stream) {
+  if (moe_status_t s = check_gemm_sizes(E, N_cap, H, I)) return s;
+  if (!word_ok(expert_offsets)) return MOE_ERR_INVALID_ARG;
+  if (!row_ok(w_gate) || !row_ok(w_up) || !row_ok(w_down)) return MOE_ERR_INVALID_ARG;
+  if (N_cap > 0 && (!row_ok(x) || !row_ok(h) || !row_ok(y))) return MOE_ERR_INVALID_ARG;
+  const size_t need = moe::gemm_workspace_bytes(E, N_cap, H, I);
+  if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 4))
+    return MOE_ERR_WORKSPACE;
+  return hip_status(moe::launch_grouped_gemm_swiglu(u16(x), expert_offsets, E, N_cap, H, I,
+                                                    u16(w_gate), u16(w_up), u16(w_down), u16(h),
+                                                    u16(y), workspace, stream));
+}
+
+// --------------------------------------------------------------------------- combine
+
+MOE_API moe_status_t moe_unpermute_combine(const void* expert_out, int64_t N,
+                                           const int32_t* row_of_slot, const int32_t* row_map,
+                                           const int32_t* expert_ids, const float* probs,
+                                           int64_t T, int32_t K, int32_t H, int32_t num_experts,
+                                           const moe_special_experts_t* special,
+                                           const void* shared_x, void* out, hipStream_t stream) {
+  if (moe_status_t s = check_tk(T, K)) return s;
+  if (moe_status_t s = check_h(H)) return s;
+  if (num_experts < 1 || N < 0 || N > INT32_MAX) return MOE_ERR_INVALID_ARG;
+  moe::SpecialArgs sp{0, 0, 0, nullptr, nullptr, nullptr, 0, 0, 0, nullptr};
+  if (special != nullptr) {
+    if (special->num_zero < 0 || special->num_copy < 0 || special->num_const < 0)
+      return MOE_ERR_INVALID_ARG;
+    const int64_t ids_total = int64_t(num_experts) + special->num_zero + special->num_copy +
+                              special->num_const;
+    if (ids_total >= INT32_MAX) return MOE_ERR_INVALID_ARG;
+    sp.num_zero = special->num_zero;
+    sp.num_copy = special->num_copy;
+    sp.num_const = special->num_const;
+    if (sp.num_copy + sp.num_const > 0) {
+      if (T > 0 && !row_ok(special->ori_x)) return MOE_ERR_INVALID_ARG;
+      sp.ori_x = u16(special->ori_x);
+    }
+    if (sp.num_const > 0) {
+      if (!word_ok(special->alpha1) || !word_ok(special->alpha2) || !row_ok(special->const_v))
+        return MOE_ERR_INVALID_ARG;
+      sp.alpha1 = special->alpha1;
+      sp.alpha2 = special->alpha2;
+      sp.a_st = special->alpha_stride_t;
+      sp.a_sc = special->alpha_stride_c;
+      sp.a_sh = special->alpha_stride_h;
+      sp.const_v = u16(special->const_v);
+    }
+  }
+  if (T > 0) {
+    if (!word_ok(row_of_slot) || !word_ok(expert_ids) || !word_ok(probs) || !row_ok(out))
+      return MOE_ERR_INVALID_ARG;
+    if (N > 0 && !row_ok(expert_out)) return MOE_ERR_INVALID_ARG;
+    if (row_map != nullptr && !aligned(row_map, 4)) return MOE_ERR_INVALID_ARG;
+    if (shared_x != nullptr && !aligned(shared_x, 16)) return MOE_ERR_INVALID_ARG;
+  }
+  return hip_status(moe::launch_combine(u16(expert_out), N, row_of_slot, row_map, expert_ids,
+                                        probs, T, K, H, num_experts, sp, u16(shared_x), u16(out),
+                                        stream));
+}
+
+// --------------------------------------------------------------------------- backward
+
+MOE_API moe_status_t moe_unpermute_grad(const void* grad_out, const void* permuted, int64_t N,
+                                        const int32_t* row_of_slot, const float* probs,
+                                        int64_t T, int32_t K, int32_t H, void* d_permuted,
+                                        float* d_probs, hipStream_t stream) {
+  if (moe_status_t s = check_tk(T, K)) return s;
+  if (moe_status_t s = check_h(H)) return s;
+  if (N < 0 || N > INT32_MAX) return MOE_ERR_INVALID_ARG;
+  if (T > 0) {
+    if (!row_ok(grad_out) || !word_ok(row_of_slot) || !word_ok(probs) || !word_ok(d_probs))
+      return MOE_ERR_INVALID_ARG;
+    if (N > 0 && (!row_ok(permuted) || !row_ok(d_permuted))) return MOE_ERR_INVALID_ARG;
+  }
+  return hip_status(moe::launch_unpermute_grad(u16(grad_out), u16(permuted), N, row_of_slot,
+                                               probs, T, K, H, u16(d_permuted), d_probs, stream));
+}

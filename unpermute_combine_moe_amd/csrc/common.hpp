@@ -1,0 +1,110 @@
+// Device helpers shared by the libmoeperm kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+// 16-byte vector of 8 bf16 values, moved as four dwords.
+struct alignas(16) Vec8 {
+  uint32_t w[4];
+};
+
+__device__ __forceinline__ Vec8 load16(const void* p) {
+  const uint4 v = *reinterpret_cast<const uint4*>(p);
+  return Vec8{{v.x, v.y, v.z, v.w}};
+}
+
+__device__ __forceinline__ void store16(void* p, const Vec8& v) {
+  *reinterpret_cast<uint4*>(p) = make_uint4(v.w[0], v.w[1], v.w[2], v.w[3]);
+}
+
+// Non-temporal variants for streams that are written once and not re-read soon.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void store16_nt(void* p, const Vec8& v) {
+  u32x4_t u = {v.w[0], v.w[1], v.w[2], v.w[3]};
+  __builtin_nontemporal_store(u, reinterpret_cast<u32x4_t*>(p));
+}
+
+__device__ __forceinline__ Vec8 load16_nt(const void* p) {
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return Vec8{{v.x, v.y, v.z, v.w}};
+}
+
+// bf16 bits -> fp32 (exact).
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ void unpack8(const Vec8& v, float f[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = bf16_lo(v.w[i]);
+    f[2 * i + 1] = bf16_hi(v.w[i]);
+  }
+}
+
+// fp32 -> bf16 bits, round to nearest, ties to even. NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return ((u >> 16) | 0x40u) & 0xFFFFu;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+__device__ __forceinline__ Vec8 pack8(const float f[8]) {
+  Vec8 v;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v.w[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+  return v;
+}
+
+// Correctly rounded bf16 of the exact product a*b where a is fp32 and b is a
+// bf16 value (so the exact product has at most 32 significant bits). The
+// fp32 product r is rounded once; its residual e = a*b - r is exact (fma).
+// r can only sit on the wrong side of a bf16 rounding boundary when r lands
+// exactly on a bf16 midpoint; the sign of e then decides the direction.
+__device__ __forceinline__ uint32_t mul_to_bf16_exact(float a, float b) {
+  const float r = a * b;
+  const float e = __builtin_fmaf(a, b, -r);
+  const uint32_t u = __float_as_uint(r);
+  if ((u & 0xFFFFu) == 0x8000u && e != 0.0f && (u & 0x7F800000u) != 0x7F800000u) {
+    // exact value is beyond the midpoint (away from zero) when e has r's sign
+    const bool away = (e > 0.0f) == (r > 0.0f);
+    return away ? ((u >> 16) + 1u) & 0xFFFFu : (u >> 16);
+  }
+  return f32_to_bf16_rne(r);
+}
+
+// Wave-uniform value (readfirstlane), for addresses the compiler should keep scalar.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Number of set bits of m strictly below this lane.
+__device__ __forceinline__ int rank_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0));
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+// Wave-wide sum of a float (butterfly over all 64 lanes).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+__host__ __device__ constexpr int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace moe

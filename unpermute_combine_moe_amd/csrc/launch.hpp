@@ -1,0 +1,45 @@
+// Internal launchers behind the C ABI. Arguments are already validated by the
+// API layer; every launcher only enqueues on `st` and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+size_t permute_workspace_bytes(int64_t T, int K, int E);
+hipError_t launch_permute(const uint16_t* x, const int32_t* ids, int64_t T, int H, int K, int E,
+                          uint16_t* permuted, int32_t* sorted_slot, int32_t* row_of_slot,
+                          int32_t* counts, int32_t* offsets, void* ws, hipStream_t st);
+
+size_t reorder_workspace_bytes(int R, int E_local);
+hipError_t launch_reorder(const uint16_t* x, const int32_t* counts, int R, int E_local, int64_t N,
+                          int H, uint16_t* y, int32_t* perm, int32_t* inv_perm,
+                          int32_t* tokens_per_expert, int32_t* offsets, void* ws, hipStream_t st);
+
+struct SpecialArgs {
+  int num_zero, num_copy, num_const;
+  const uint16_t* ori_x;
+  const float* alpha1;
+  const float* alpha2;
+  int64_t a_st, a_sc, a_sh;
+  const uint16_t* const_v;
+};
+
+hipError_t launch_combine(const uint16_t* expert_out, int64_t N, const int32_t* row_of_slot,
+                          const int32_t* row_map, const int32_t* ids, const float* probs,
+                          int64_t T, int K, int H, int E, const SpecialArgs& sp,
+                          const uint16_t* shared_x, uint16_t* out, hipStream_t st);
+
+hipError_t launch_unpermute_grad(const uint16_t* grad_out, const uint16_t* permuted, int64_t N,
+                                 const int32_t* row_of_slot, const float* probs, int64_t T, int K,
+                                 int H, uint16_t* d_permuted, float* d_probs, hipStream_t st);
+
+size_t gemm_workspace_bytes(int E, int64_t N_cap, int H, int I);
+hipError_t launch_grouped_gemm_swiglu(const uint16_t* x, const int32_t* offsets, int E,
+                                      int64_t N_cap, int H, int I, const uint16_t* wg,
+                                      const uint16_t* wu, const uint16_t* wd, uint16_t* h,
+                                      uint16_t* y, void* ws, hipStream_t st);
+
+}  // namespace moe

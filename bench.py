@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--no-ops", action="store_true", help="skip the per-workload op table")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=1536)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="N",
+                    help="only run N device copies of 256 MiB (counter calibration) and exit")
     return ap.parse_args()
 
 
@@ -336,6 +338,14 @@ def main():
     moe.load()
     dev = torch.device("cuda:0")
     log(f"device: {torch.cuda.get_device_name(0)}")
+    if args.copy_probe:
+        a = torch.ones(1 << 27, dtype=torch.bfloat16, device=dev)   # 256 MiB
+        b = torch.empty_like(a)
+        for _ in range(args.copy_probe):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"copy probe: {args.copy_probe} x 256 MiB read + 256 MiB written")
+        return
 
     d, wall, seg, n_rows = run_layer(args, dev)
     c = d["cfg"]

@@ -58,3 +58,15 @@ def ulp_diff(a_bits: np.ndarray, b_bits: np.ndarray) -> int:
     if a_bits.size == 0:
         return 0
     return int(np.max(np.abs(key(a_bits) - key(b_bits))))
+
+
+def assert_h_within_ulp(h_bits: np.ndarray, h_ref: np.ndarray, what: str = "h"):
+    """h is stored as bf16: it must sit within one bf16 ulp (2^-8 relative) of
+    the fp64 value, plus a small absolute term for the fp32 accumulation of
+    g and u."""
+    got = f64(h_bits)
+    rms = float(np.sqrt(np.mean(h_ref ** 2))) if h_ref.size else 0.0
+    err = np.abs(got - h_ref)
+    bound = 2.0 ** -8 * np.abs(h_ref) + 1e-4 * rms
+    bad = err > bound
+    assert not bad.any(), f"{what}: {int(bad.sum())} elements beyond one bf16 ulp; worst {err.max():.3e}"

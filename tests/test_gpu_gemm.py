@@ -6,7 +6,7 @@ import torch
 
 import moe_workloads as W
 import oracle
-from helpers import bits, f64, gemm_tol, to_dev, to_dev_bf16
+from helpers import assert_h_within_ulp, bits, f64, gemm_tol, to_dev, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -37,17 +37,17 @@ def test_gemm_small(moe_lib, counts, H, I, seed):
     off = _offsets(counts)
     N = int(off[-1]) + 3                           # capacity rows past the last expert
     x = W.normal_bf16(rng, (N, H))
-    wg = W.normal_bf16(rng, (E, H, I), 0.05)
-    wu = W.normal_bf16(rng, (E, H, I), 0.05)
-    wd = W.normal_bf16(rng, (E, I, H), 0.05)
+    # the weight scale of the workloads, N(0, 0.02^2): the y bound is stated for it
+    wg = W.normal_bf16(rng, (E, H, I), 0.02)
+    wu = W.normal_bf16(rng, (E, H, I), 0.02)
+    wd = W.normal_bf16(rng, (E, I, H), 0.02)
     hb, yb = _gemm(moe_lib, x, off, wg, wu, wd)
     n = int(off[-1])
     if n == 0:
         return
     h_ref, y_ref = oracle.grouped_swiglu(x[:n], off, wg, wu, wd)
-    tol = gemm_tol(H)
-    assert np.max(np.abs(f64(hb[:n]) - h_ref)) <= tol
-    assert np.max(np.abs(f64(yb[:n]) - y_ref)) <= tol
+    assert np.max(np.abs(f64(yb[:n]) - y_ref)) <= gemm_tol(H)
+    assert_h_within_ulp(hb[:n], h_ref)
 
 
 def test_gemm_config1(moe_lib):
@@ -62,7 +62,7 @@ def test_gemm_config1(moe_lib):
     err = np.max(np.abs(f64(yb) - y_ref))
     print(f"config 1: max |y - ref| = {err:.3e} (bound {tol:.3e})")
     assert err <= tol
-    assert np.max(np.abs(f64(hb) - h_ref)) <= tol
+    assert_h_within_ulp(hb, h_ref)
 
 
 def test_gemm_config3_sampled(moe_lib):
@@ -86,9 +86,12 @@ def test_gemm_config3_sampled(moe_lib):
     row_e = np.searchsorted(off, rows, side="right") - 1
     tol = gemm_tol(c["H"])
     worst = 0.0
+    h_refs = []
     for r, e in zip(rows, row_e):
         h_ref, y_ref = oracle.swiglu_row(p["permuted"][r], g["w_gate"][e], g["w_up"][e],
                                          g["w_down"][e])
-        worst = max(worst, np.max(np.abs(f64(yb[r]) - y_ref)), np.max(np.abs(f64(hb[r]) - h_ref)))
-    print(f"config 3: {len(rows)} sampled rows, max err {worst:.3e} (bound {tol:.3e})")
+        worst = max(worst, float(np.max(np.abs(f64(yb[r]) - y_ref))))
+        h_refs.append(h_ref)
+    print(f"config 3: {len(rows)} sampled rows, max |y - ref| {worst:.3e} (bound {tol:.3e})")
     assert worst <= tol
+    assert_h_within_ulp(hb[rows], np.stack(h_refs))

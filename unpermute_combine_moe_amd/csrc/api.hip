@@ -5,6 +5,8 @@
 
 #include <limits.h>
 
+#include <algorithm>
+
 #include "launch.hpp"
 
 #define MOE_API extern "C" __attribute__((visibility("default")))
@@ -130,6 +132,10 @@ moe_status_t check_gemm_sizes(int32_t E, int64_t N_cap, int32_t H, int32_t I) {
   if (N_cap < 0 || N_cap > INT32_MAX) return MOE_ERR_INVALID_ARG;
   if (H <= 0 || I <= 0) return MOE_ERR_INVALID_ARG;
   if (H % 64 != 0 || I % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  // the kernel indexes (row tile, column tile) pairs with 32-bit integers
+  const int64_t max_row_tiles = N_cap / 128 + E + 1;
+  const int64_t max_col_tiles = (std::max(H, I) + 127) / 128;
+  if (max_row_tiles * max_col_tiles >= INT32_MAX) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 }  // namespace

@@ -14,16 +14,27 @@
 // same XCD and reuse its L2.
 //
 // Tile: BM = 128 rows x 256 B-columns x BK = 64, 256 threads as 2 x 2 waves;
-// each wave owns 64 rows x 128 B-columns = 2 x 4 MFMA 32x32 accumulators.
+// each wave owns 64 rows x 128 B-columns = 2 x 4 MFMA 32x32 accumulators. The
+// MFMA is fed the weight fragment as its first operand, i.e. it computes the
+// transposed tile, so that each lane ends up with four consecutive output
+// columns of one token row (8-byte stores in the epilogue).
 // Pass 1 packs 128 gate columns and the matching 128 up columns into the 256
 // B-columns, so the SwiGLU epilogue finds g and u of an output element in the
-// same lane and register. The weights are [K][N] (N contiguous); MFMA operands
-// want 8 consecutive k per lane, so each thread loads an 8(k) x 8(n) block and
-// transposes it in registers before writing it to LDS. LDS tiles are [row][k]
-// in 16-byte chunks with the chunk index XOR-swizzled by (row & 7), which
-// keeps both the transposed writes and the MFMA operand reads free of bank
-// conflicts. Two LDS stages; the next k-step's global loads are in flight
-// while the current one is multiplied.
+// same lane and register.
+//
+// Data path: both operand tiles go from global memory straight into LDS
+// (global_load_lds_dwordx4, 16 bytes per lane, no register staging) through a
+// three-stage ring, so two k-steps of loads are in flight while one is
+// multiplied; one s_barrier per k-step, with explicit vmcnt waits. A is kept
+// [row][k] and read with ds_read_b128. The weights stay in their [k][n]
+// layout in LDS and the MFMA B operand (8 consecutive k of one column per
+// lane) is formed by two ds_read_b64_tr_b16 transpose reads: within each group
+// of 16 lanes, output lane 4a+b takes element b of input lanes a, a+4, a+8,
+// a+12, so input lane i points at row k0 + i/4, column 4*(i%4).
+// Both tiles are stored in 16-byte chunks with an XOR swizzle of the chunk
+// index (A: by row & 7, B: by 4 * (k & 3)) that keeps the operand reads free of
+// bank conflicts; the swizzle is applied by choosing which global chunk each
+// lane loads, since a direct-to-LDS load writes lane L at base + 16 L.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -40,6 +51,7 @@ constexpr int kThreads = 256;
 constexpr int kChunksA = BM * BK / 8;  // 16-byte chunks per stage
 constexpr int kChunksB = BN * BK / 8;
 constexpr int kSchedThreads = 1024;
+constexpr int kMaxExperts = 1024;
 constexpr int kXcds = 8;
 
 __device__ __forceinline__ int swz(int row, int kc) { return row * (BK / 8) + (kc ^ (row & 7)); }
@@ -78,8 +90,50 @@ k_gemm_sched(const int32_t* __restrict__ offsets, int E, int64_t N_cap, int32_t*
   }
 }
 
-__device__ __forceinline__ bf16x8_t lds_frag(const uint4* base, int idx) {
-  const uint4 v = base[idx];
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
+
+constexpr int kStages = 3;
+constexpr int kLoadsA = kChunksA / kThreads;  // direct-to-LDS loads per thread per stage
+constexpr int kLoadsB = kChunksB / kThreads;
+constexpr int kLoadsPerStage = kLoadsA + kLoadsB;
+constexpr int kStageBytes = (kChunksA + kChunksB) * 16;
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// 16-byte direct global -> LDS load: this lane's 16 bytes land at LDS byte
+// address lds_base + 16 * lane. Issued as inline asm so the compiler does not
+// treat it as an LDS write it must wait for before every later LDS read; the
+// kernel orders these loads itself with wait_vmcnt and stage_barrier.
+__device__ __forceinline__ void load_lds16(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds_base), "v"(gptr)
+               : "memory", "m0");
+}
+
+// Workgroup barrier without a memory fence (a fence would also wait for the
+// loads still in flight); the "memory" clobber keeps the compiler from moving
+// LDS accesses across it.
+__device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Same, after this wave's own LDS reads have returned (so a stage it has read
+// may be refilled by any wave once everyone is past the barrier).
+__device__ __forceinline__ void reads_done_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ int swz_b(int k, int c) { return k * (BN / 8) + (c ^ (4 * (k & 3))); }
+
+__device__ __forceinline__ bf16x8_t lds_read_a(const lds_u8_t* base, int slot) {
+  const u32x4_t v = *(const __attribute__((address_space(3))) u32x4_t*)(base + slot * 16);
   bf16x8_t r;
   __builtin_memcpy(&r, &v, 16);
   return r;
@@ -91,174 +145,244 @@ __global__ void __launch_bounds__(kThreads, 1)
 k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0,
        const uint16_t* __restrict__ B1, int Ncols, const int32_t* __restrict__ ws, int E,
        uint16_t* __restrict__ C) {
-  __shared__ uint4 sA[2][kChunksA];
-  __shared__ uint4 sB[2][kChunksB];
-
-  const int32_t* prefix = ws;
-  const int32_t* offs = ws + (E + 1);
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes];
+  // row-tile prefix and clamped expert offsets, staged once per workgroup so the
+  // per-tile expert lookup is a binary search in LDS
+  __shared__ int32_t s_prefix[kMaxExperts + 1];
+  __shared__ int32_t s_offs[kMaxExperts + 1];
+  lds_u8_t* lds = (lds_u8_t*)(smem);
+  for (int i = threadIdx.x; i <= E; i += kThreads) {
+    s_prefix[i] = ws[i];
+    s_offs[i] = ws[E + 1 + i];
+  }
+  __syncthreads();
+  const int32_t* prefix = s_prefix;
+  const int32_t* offs = s_offs;
   const int tid = threadIdx.x;
   const int lane = tid % kWave;
   const int wave = tid / kWave;
   const int wm = wave & 1;   // 64-row half of the tile
   const int wn = wave >> 1;  // B-column half
 
-  // columns of output produced per tile
   constexpr int kOutCols = (kMode == 0) ? BN / 2 : BN;
   const int col_tiles = (Ncols + kOutCols - 1) / kOutCols;
   const int row_tiles = prefix[E];
-  const int64_t total = int64_t(row_tiles) * col_tiles;
+  const int total = row_tiles * col_tiles;  // < 2^31: at most (2^31 / 128 + 1024) * 32
 
   // XCD-aware split of the logical tile space: workgroup b runs on XCD b % 8.
   const int G = gridDim.x;
   const int xcd = blockIdx.x % kXcds;
   const int per_xcd = G / kXcds;
-  const int64_t t_lo = total * xcd / kXcds;
-  const int64_t t_hi = total * (xcd + 1) / kXcds;
-
-  const int a_kc = tid % 8;        // A loader: chunk column and first row
-  const int a_r0 = tid / 8;        // rows a_r0 + 32 i
-  const int b_kg = tid % 8;        // B loader: 8-row k group
-  const int b_ng = tid / 8;        // B loader: 8-column group 0..31
+  const int t_lo = static_cast<int>(int64_t(total) * xcd / kXcds);
+  const int t_hi = static_cast<int>(int64_t(total) * (xcd + 1) / kXcds);
   const int ksteps = Kdim / BK;
 
-  for (int64_t tile = t_lo + blockIdx.x / kXcds; tile < t_hi; tile += per_xcd) {
-    const int rt = static_cast<int>(tile / col_tiles);
-    const int ct = static_cast<int>(tile % col_tiles);
-    // expert owning row tile rt: last e with prefix[e] <= rt
-    int lo = 0, hi = E;
+  // LDS byte offsets (within a stage) of this lane's B-operand transpose reads
+  // for sub-step 0; sub-step kk adds 16 rows, which keeps k & 3 and the swizzle
+  int b_off[4][2];  // [n-frag][half]
+  const int g16 = lane / 16, i16 = lane % 16;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    int ncol;
+    if (kMode == 0) ncol = (j < 2 ? 0 : BN / 2) + wn * 64 + (j % 2) * 32;
+    else ncol = wn * 128 + j * 32;
+    const int n = ncol + 16 * (g16 % 2) + 4 * (i16 % 4);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int k = 8 * (g16 / 2) + i16 / 4 + 4 * half;  // + 16 * kk at use (k & 3 unchanged)
+      b_off[j][half] = kChunksA * 16 + swz_b(k, n / 8) * 16 + (n % 8) * 2;
+    }
+  }
+
+  // This workgroup's tiles: first, first + per_xcd, ... inside [t_lo, t_hi).
+  // The k-steps of all of them form one sequence s = j * ksteps + ks, and the
+  // loads run two steps ahead of the multiply across tile boundaries, so the
+  // next tile's first stages are in flight during this tile's epilogue.
+  const int first = t_lo + static_cast<int>(blockIdx.x) / kXcds;
+  const int ntiles = (first < t_hi) ? (t_hi - 1 - first) / per_xcd + 1 : 0;
+  const int nsteps = ntiles * ksteps;
+
+  struct TileInfo {
+    int e, row0, row_end, n0;
+  };
+  auto tile_info = [&](int j) {
+    const int tile = first + j * per_xcd;
+    const int rt = tile / col_tiles;
+    const int ct = tile - rt * col_tiles;
+    int lo = 0, hi = E;  // expert owning row tile rt: last e with prefix[e] <= rt
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (prefix[mid] <= rt) lo = mid; else hi = mid;
     }
-    const int e = lo;
-    const int row0 = offs[e] + (rt - prefix[e]) * BM;
-    const int row_end = std::min(row0 + BM, offs[e + 1]);
-    const int n0 = ct * kOutCols;
+    TileInfo t;
+    t.e = lo;
+    t.row0 = offs[lo] + (rt - prefix[lo]) * BM;
+    t.row_end = std::min(t.row0 + BM, offs[lo + 1]);
+    t.n0 = ct * kOutCols;
+    return t;
+  };
 
-    // A loader rows (clamped into the tile's valid rows; extra rows are never stored)
-    const uint16_t* a_ptr[4];
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+  // Load cursor: tile index lj and k-step lk of the next stage to issue, with the
+  // global sources of this thread's loads for tile lj precomputed (each k-step
+  // only adds its k offset).
+  int lj = 0;
+  int lk = 0;
+  int lbuf = 0;
+  const uint16_t* a_src[kLoadsA];
+  const uint16_t* b_src[kLoadsB];
+  auto load_tile_sources = [&](int j) {
+    const TileInfo t = tile_info(j);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = std::min(row0 + a_r0 + 32 * i, row_end - 1);
-      a_ptr[i] = A + int64_t(r) * Kdim + a_kc * 8;
+    for (int i = 0; i < kLoadsA; ++i) {
+      const int slot = i * kThreads + wave * kWave + lane;
+      const int m = slot >> 3;
+      const int kc = (slot & 7) ^ (m & 7);
+      const int r = std::min(t.row0 + m, t.row_end - 1);
+      a_src[i] = A + int64_t(r) * Kdim + kc * 8;
     }
-    // B loader column base for this thread
-    const uint16_t* b_ptr;
-    bool b_valid;
-    {
-      int col;
+#pragma unroll
+    for (int i = 0; i < kLoadsB; ++i) {
+      const int slot = i * kThreads + wave * kWave + lane;
+      const int k = slot >> 5;
+      const int c = (slot & 31) ^ (4 * (k & 3));
       const uint16_t* base;
+      int col;
       if (kMode == 0) {
-        base = (b_ng < 16) ? B0 : B1;
-        col = n0 + (b_ng % 16) * 8;
+        base = (c < 16) ? B0 : B1;
+        col = t.n0 + (c % 16) * 8;
       } else {
         base = B0;
-        col = n0 + b_ng * 8;
+        col = t.n0 + c * 8;
       }
-      b_valid = col < Ncols;
-      b_ptr = base + int64_t(e) * Kdim * Ncols + int64_t(b_kg * 8) * Ncols + (b_valid ? col : 0);
+      if (col >= Ncols) col = 0;  // columns past the matrix: any valid address, never stored
+      b_src[i] = base + int64_t(t.e) * Kdim * Ncols + int64_t(k) * Ncols + col;
     }
+  };
+  auto issue_next = [&]() {
+    if (lk == 0) load_tile_sources(lj);
+    const uint32_t st = uniform(static_cast<int>(lds0 + lbuf * kStageBytes + wave * kWave * 16));
+#pragma unroll
+    for (int i = 0; i < kLoadsA; ++i) load_lds16(a_src[i] + lk * BK, st + i * kThreads * 16);
+#pragma unroll
+    for (int i = 0; i < kLoadsB; ++i)
+      load_lds16(b_src[i] + int64_t(lk) * BK * Ncols, st + (kChunksA + i * kThreads) * 16);
+    lbuf = (lbuf + 1 == kStages) ? 0 : lbuf + 1;
+    if (++lk == ksteps) {
+      lk = 0;
+      ++lj;
+    }
+  };
 
-    Vec8 ra[4], rb[8];
-    auto gload = [&](int ks) {
-      const int64_t k0 = int64_t(ks) * BK;
+  // operand fragments of one 16-wide k sub-step of the stage at `st`
+  auto read_frags = [&](const lds_u8_t* st, int kk, bf16x8_t fa[2], bf16x8_t fb[4]) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ra[i] = load16(a_ptr[i] + k0);
+    for (int i = 0; i < 2; ++i)
+      fa[i] = lds_read_a(st, swz(wm * 64 + i * 32 + lane % 32, kk * 2 + lane / 32));
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (b_valid) rb[j] = load16(b_ptr + (k0 + j) * Ncols);
-        else rb[j] = Vec8{{0u, 0u, 0u, 0u}};
-      }
-    };
-    auto lstore = [&](int buf) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = a_r0 + 32 * i;
-        sA[buf][swz(r, a_kc)] = make_uint4(ra[i].w[0], ra[i].w[1], ra[i].w[2], ra[i].w[3]);
-      }
-      // 8x8 transpose: column c of the thread's block gets k = b_kg*8 .. +8
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const int w = c >> 1;
-        const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-        uint4 o;
-        o.x = __builtin_amdgcn_perm(rb[1].w[w], rb[0].w[w], sel);
-        o.y = __builtin_amdgcn_perm(rb[3].w[w], rb[2].w[w], sel);
-        o.z = __builtin_amdgcn_perm(rb[5].w[w], rb[4].w[w], sel);
-        o.w = __builtin_amdgcn_perm(rb[7].w[w], rb[6].w[w], sel);
-        const int n = b_ng * 8 + c;
-        sB[buf][swz(n, b_kg)] = o;
-      }
-    };
+    for (int jj = 0; jj < 4; ++jj) {
+      const v4i16_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_v4i16_t*)(st + b_off[jj][0] + kk * 16 * (BN * 2)));
+      const v4i16_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_v4i16_t*)(st + b_off[jj][1] + kk * 16 * (BN * 2)));
+      __builtin_memcpy(&fb[jj], &lo4, 8);
+      __builtin_memcpy(reinterpret_cast<char*>(&fb[jj]) + 8, &hi4, 8);
+    }
+  };
 
+  // Schedule of one k-step (one wave per SIMD, in-order issue): the LDS reads
+  // of sub-step kk + 1 are issued before the MFMAs of sub-step kk, and during
+  // the last sub-step the wave already waits for the next stage, passes the
+  // barrier, issues the next loads and reads the next stage's first
+  // fragments. sched_barrier keeps the compiler from regrouping them.
+  int issued = 0;
+  for (; issued < nsteps && issued < kStages - 1; ++issued) issue_next();
+  bf16x8_t fa[2][2], fb[2][4];
+  if (nsteps > 0) {
+    if (issued > 1) wait_vmcnt<kLoadsPerStage>();
+    else wait_vmcnt<0>();
+    stage_barrier();
+    if (issued < nsteps) {
+      issue_next();
+      ++issued;
+    }
+    read_frags(lds, 0, fa[0], fb[0]);
+  }
+  int s = 0;  // global k-step being multiplied
+  int cbuf = 0;
+  for (int j = 0; j < ntiles; ++j) {
+    const TileInfo ci = tile_info(j);
     f32x16_t acc[2][4];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+        for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.f;
 
-    // B-column of each of the wave's four n-fragments
-    int ncol[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (kMode == 0) ncol[j] = (j < 2 ? 0 : BN / 2) + wn * 64 + (j % 2) * 32 + lane % 32;
-      else ncol[j] = wn * 128 + j * 32 + lane % 32;
-    }
-    int mrow[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) mrow[i] = wm * 64 + i * 32 + lane % 32;
-
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int ks = 0; ks < ksteps; ++ks) {
-      const int buf = ks & 1;
-      if (ks + 1 < ksteps) gload(ks + 1);
+    for (int kstep = 0; kstep < ksteps; ++kstep, ++s) {
+      const lds_u8_t* st = lds + cbuf * kStageBytes;
+      cbuf = (cbuf + 1 == kStages) ? 0 : cbuf + 1;
 #pragma unroll
       for (int kk = 0; kk < BK / 16; ++kk) {
-        const int kc = kk * 2 + lane / 32;
-        bf16x8_t fa[2], fb[4];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) fa[i] = lds_frag(sA[buf], swz(mrow[i], kc));
-#pragma unroll
-        for (int j = 0; j < 4; ++j) fb[j] = lds_frag(sB[buf], swz(ncol[j], kc));
+        const int cur = kk & 1;
+        __builtin_amdgcn_sched_barrier(0);
+        if (kk + 1 < BK / 16) {
+          read_frags(st, kk + 1, fa[cur ^ 1], fb[cur ^ 1]);
+        } else if (s + 1 < nsteps) {
+          // stage s + 1 has landed once at most the loads issued after it are in flight
+          if (issued > s + 2) wait_vmcnt<kLoadsPerStage>();
+          else wait_vmcnt<0>();
+          reads_done_barrier();  // everyone is done reading stage s; s + 1 is visible
+          if (issued < nsteps) {
+            issue_next();  // refills stage s's buffer; may belong to the next tile
+            ++issued;
+          }
+          read_frags(lds + cbuf * kStageBytes, 0, fa[cur ^ 1], fb[cur ^ 1]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+          for (int jj = 0; jj < 4; ++jj)
+            acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cur][jj], fa[cur][i],
+                                                                 acc[i][jj], 0, 0, 0);
       }
-      if (ks + 1 < ksteps) lstore(buf ^ 1);
-      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
     }
 
-    // epilogue: lane holds column lane%32 and rows 8*(r/4) + 4*(lane/32) + r%4
+    // Epilogue. The MFMA computes the transposed product (weights as the first
+    // operand), so lane l holds token row l % 32 of its fragment and, in
+    // registers 4q .. 4q+3, the four consecutive output columns
+    // 8q + 4 (l / 32) + 0..3: one 8-byte store each, no data exchange.
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
+      const int row = ci.row0 + wm * 64 + i * 32 + lane % 32;
+      if (row >= ci.row_end) continue;
+      uint16_t* crow = C + int64_t(row) * Ncols;
+      constexpr int kOutFrags = (kMode == 0) ? 2 : 4;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = row0 + wm * 64 + i * 32 + 8 * (r / 4) + 4 * (lane / 32) + (r % 4);
-        if (row >= row_end) continue;
-        if (kMode == 0) {
+      for (int jj = 0; jj < kOutFrags; ++jj) {
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int col = n0 + wn * 64 + j * 32 + lane % 32;
-            if (col < Ncols) {
-              const float g = acc[i][j][r];
-              const float u = acc[i][j + 2][r];
-              const float hv = g / (1.0f + __expf(-g)) * u;
-              C[int64_t(row) * Ncols + col] = static_cast<uint16_t>(f32_to_bf16_rne(hv));
+        for (int q = 0; q < 4; ++q) {
+          const int col = ci.n0 + ((kMode == 0) ? wn * 64 : wn * 128) + jj * 32 + 8 * q +
+                          4 * (lane / 32);
+          if (col >= Ncols) continue;
+          float v[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            if (kMode == 0) {
+              const float g = acc[i][jj][4 * q + k];
+              const float u = acc[i][jj + 2][4 * q + k];
+              v[k] = g / (1.0f + __expf(-g)) * u;
+            } else {
+              v[k] = acc[i][jj][4 * q + k];
             }
           }
-        } else {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int col = n0 + wn * 128 + j * 32 + lane % 32;
-            if (col < Ncols)
-              C[int64_t(row) * Ncols + col] = static_cast<uint16_t>(f32_to_bf16_rne(acc[i][j][r]));
-          }
+          uint2 packed;
+          packed.x = pack_bf16x2(v[0], v[1]);
+          packed.y = pack_bf16x2(v[2], v[3]);
+          *reinterpret_cast<uint2*>(crow + col) = packed;
         }
       }
     }

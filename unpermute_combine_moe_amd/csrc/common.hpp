@@ -57,8 +57,15 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return u >> 16;
 }
 
+// Two fp32 -> packed bf16 pair (lo in bits 0..15), round to nearest even, by
+// the gfx950 conversion instruction (v_cvt_pk_bf16_f32).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+  const bf16x2_t b = __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t);
+  uint32_t u;
+  __builtin_memcpy(&u, &b, 4);
+  return u;
 }
 
 __device__ __forceinline__ Vec8 pack8(const float f[8]) {

@@ -99,6 +99,12 @@ constexpr int kLoadsA = kChunksA / kThreads;  // direct-to-LDS loads per thread 
 constexpr int kLoadsB = kChunksB / kThreads;
 constexpr int kLoadsPerStage = kLoadsA + kLoadsB;
 constexpr int kStageBytes = (kChunksA + kChunksB) * 16;
+// epilogue stores per wave per tile: 2 row fragments x output fragments x 4
+template <int kMode>
+struct EpiloguePlan {
+  static constexpr int kOutFrags = (kMode == 0) ? 2 : 4;
+  static constexpr int kStores = 2 * kOutFrags * 4;
+};
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
@@ -144,7 +150,7 @@ template <int kMode>
 __global__ void __launch_bounds__(kThreads, 1)
 k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0,
        const uint16_t* __restrict__ B1, int Ncols, const int32_t* __restrict__ ws, int E,
-       uint16_t* __restrict__ C) {
+       uint16_t* __restrict__ C, uint2* __restrict__ trash) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes];
   // row-tile prefix and clamped expert offsets, staged once per workgroup so the
   // per-tile expert lookup is a binary search in LDS
@@ -165,6 +171,8 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
   const int wn = wave >> 1;  // B-column half
 
   constexpr int kOutCols = (kMode == 0) ? BN / 2 : BN;
+  constexpr int kStoresPerTile = EpiloguePlan<kMode>::kStores;
+  static_assert(kLoadsPerStage + kStoresPerTile < 64, "vmcnt field is 6 bits");
   const int col_tiles = (Ncols + kOutCols - 1) / kOutCols;
   const int row_tiles = prefix[E];
   const int total = row_tiles * col_tiles;  // < 2^31: at most (2^31 / 128 + 1024) * 32
@@ -259,19 +267,39 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
       b_src[i] = base + int64_t(t.e) * Kdim * Ncols + int64_t(k) * Ncols + col;
     }
   };
-  auto issue_next = [&]() {
+  // The 12 loads of a stage are issued in four groups of three, one group per
+  // MFMA sub-step, so their address work hides under the matrix ops.
+  constexpr int kLoadGroups = BK / 16;
+  constexpr int kLoadsPerGroup = kLoadsPerStage / kLoadGroups;
+  static_assert(kLoadsPerStage % kLoadGroups == 0, "load groups");
+  uint32_t l_st = 0;
+  auto issue_begin = [&]() {
     if (lk == 0) load_tile_sources(lj);
-    const uint32_t st = uniform(static_cast<int>(lds0 + lbuf * kStageBytes + wave * kWave * 16));
+    l_st = uniform(static_cast<int>(lds0 + lbuf * kStageBytes + wave * kWave * 16));
+  };
+  auto issue_group = [&](int grp) {
 #pragma unroll
-    for (int i = 0; i < kLoadsA; ++i) load_lds16(a_src[i] + lk * BK, st + i * kThreads * 16);
-#pragma unroll
-    for (int i = 0; i < kLoadsB; ++i)
-      load_lds16(b_src[i] + int64_t(lk) * BK * Ncols, st + (kChunksA + i * kThreads) * 16);
+    for (int g = 0; g < kLoadsPerGroup; ++g) {
+      const int i = grp * kLoadsPerGroup + g;
+      if (i < kLoadsA)
+        load_lds16(a_src[i] + lk * BK, l_st + i * kThreads * 16);
+      else
+        load_lds16(b_src[i - kLoadsA] + int64_t(lk) * BK * Ncols,
+                   l_st + (kChunksA + (i - kLoadsA) * kThreads) * 16);
+    }
+  };
+  auto issue_end = [&]() {
     lbuf = (lbuf + 1 == kStages) ? 0 : lbuf + 1;
     if (++lk == ksteps) {
       lk = 0;
       ++lj;
     }
+  };
+  auto issue_next = [&]() {
+    issue_begin();
+#pragma unroll
+    for (int grp = 0; grp < kLoadGroups; ++grp) issue_group(grp);
+    issue_end();
   };
 
   // operand fragments of one 16-wide k sub-step of the stage at `st`
@@ -290,11 +318,14 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
     }
   };
 
-  // Schedule of one k-step (one wave per SIMD, in-order issue): the LDS reads
-  // of sub-step kk + 1 are issued before the MFMAs of sub-step kk, and during
-  // the last sub-step the wave already waits for the next stage, passes the
-  // barrier, issues the next loads and reads the next stage's first
-  // fragments. sched_barrier keeps the compiler from regrouping them.
+  // Schedule of one k-step (one wave per SIMD, in-order issue). Stage t's
+  // loads are issued during step t - 2, spread over its four MFMA sub-steps,
+  // into the buffer that step t - 3 used (free since the barrier that ended
+  // step t - 3's reads). During sub-step kk the wave first issues the LDS
+  // reads of sub-step kk + 1 and its share of the loads, then the MFMAs of
+  // sub-step kk. Before the last sub-step's MFMAs it waits for the next stage,
+  // passes the barrier and reads the next stage's first fragments.
+  // sched_barrier keeps the compiler from regrouping these.
   int issued = 0;
   for (; issued < nsteps && issued < kStages - 1; ++issued) issue_next();
   bf16x8_t fa[2][2], fb[2][4];
@@ -302,14 +333,11 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
     if (issued > 1) wait_vmcnt<kLoadsPerStage>();
     else wait_vmcnt<0>();
     stage_barrier();
-    if (issued < nsteps) {
-      issue_next();
-      ++issued;
-    }
     read_frags(lds, 0, fa[0], fb[0]);
   }
   int s = 0;  // global k-step being multiplied
   int cbuf = 0;
+  int epi_step = -8;  // k-step after which the last epilogue ran
   for (int j = 0; j < ntiles; ++j) {
     const TileInfo ci = tile_info(j);
     f32x16_t acc[2][4];
@@ -323,21 +351,29 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
     for (int kstep = 0; kstep < ksteps; ++kstep, ++s) {
       const lds_u8_t* st = lds + cbuf * kStageBytes;
       cbuf = (cbuf + 1 == kStages) ? 0 : cbuf + 1;
+      const bool loads_now = issued < nsteps;  // stage s + 2 goes out during this step
+      if (loads_now) issue_begin();
 #pragma unroll
       for (int kk = 0; kk < BK / 16; ++kk) {
         const int cur = kk & 1;
         __builtin_amdgcn_sched_barrier(0);
         if (kk + 1 < BK / 16) {
           read_frags(st, kk + 1, fa[cur ^ 1], fb[cur ^ 1]);
+          if (loads_now) issue_group(kk);
+          if (loads_now && kk + 2 == BK / 16) issue_group(kk + 1);
         } else if (s + 1 < nsteps) {
-          // stage s + 1 has landed once at most the loads issued after it are in flight
-          if (issued > s + 2) wait_vmcnt<kLoadsPerStage>();
-          else wait_vmcnt<0>();
-          reads_done_barrier();  // everyone is done reading stage s; s + 1 is visible
-          if (issued < nsteps) {
-            issue_next();  // refills stage s's buffer; may belong to the next tile
-            ++issued;
+          // Stage s + 1 has landed once at most the vector-memory operations
+          // issued after its loads are in flight (the counter completes loads
+          // and stores in issue order): stage s + 2's loads, if issued, and
+          // the stores of an epilogue that ran right after step s - 1.
+          const bool next_loads = issued + (loads_now ? 1 : 0) > s + 2;
+          if (epi_step != s - 1) {
+            if (next_loads) wait_vmcnt<kLoadsPerStage>(); else wait_vmcnt<0>();
+          } else {
+            if (next_loads) wait_vmcnt<kLoadsPerStage + kStoresPerTile>();
+            else wait_vmcnt<kStoresPerTile>();
           }
+          reads_done_barrier();  // everyone is done reading stage s; s + 1 is visible
           read_frags(lds + cbuf * kStageBytes, 0, fa[cur ^ 1], fb[cur ^ 1]);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -349,17 +385,18 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
                                                                  acc[i][jj], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
+      if (loads_now) {
+        issue_end();
+        ++issued;
+      }
     }
 
-    // Epilogue. The MFMA computes the transposed product (weights as the first
-    // operand), so lane l holds token row l % 32 of its fragment and, in
-    // registers 4q .. 4q+3, the four consecutive output columns
-    // 8q + 4 (l / 32) + 0..3: one 8-byte store each, no data exchange.
+    epi_step = s - 1;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int row = ci.row0 + wm * 64 + i * 32 + lane % 32;
-      if (row >= ci.row_end) continue;
-      uint16_t* crow = C + int64_t(row) * Ncols;
+      const bool row_ok = row < ci.row_end;
+      uint16_t* crow = C + int64_t(row_ok ? row : 0) * Ncols;
       constexpr int kOutFrags = (kMode == 0) ? 2 : 4;
 #pragma unroll
       for (int jj = 0; jj < kOutFrags; ++jj) {
@@ -367,14 +404,13 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
         for (int q = 0; q < 4; ++q) {
           const int col = ci.n0 + ((kMode == 0) ? wn * 64 : wn * 128) + jj * 32 + 8 * q +
                           4 * (lane / 32);
-          if (col >= Ncols) continue;
           float v[4];
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
             if (kMode == 0) {
               const float g = acc[i][jj][4 * q + k];
               const float u = acc[i][jj + 2][4 * q + k];
-              v[k] = g / (1.0f + __expf(-g)) * u;
+              v[k] = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
             } else {
               v[k] = acc[i][jj][4 * q + k];
             }
@@ -382,7 +418,9 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
           uint2 packed;
           packed.x = pack_bf16x2(v[0], v[1]);
           packed.y = pack_bf16x2(v[2], v[3]);
-          *reinterpret_cast<uint2*>(crow + col) = packed;
+          uint2* dst = (row_ok && col < Ncols) ? reinterpret_cast<uint2*>(crow + col)
+                                               : trash + lane;
+          *dst = packed;
         }
       }
     }
@@ -401,8 +439,12 @@ int persistent_grid() {
 
 }  // namespace
 
+// ws layout: tile_prefix[E+1] | offs[E+1] (int32), then at kTrashOffset(E) a
+// 512-byte area that absorbs the epilogue stores of lanes without a valid row
+size_t trash_offset(int E) { return ((static_cast<size_t>(2 * (E + 1)) * 4 + 255) / 256) * 256; }
+
 size_t gemm_workspace_bytes(int E, int64_t /*N_cap*/, int /*H*/, int /*I*/) {
-  return static_cast<size_t>(2 * (E + 1)) * sizeof(int32_t);
+  return trash_offset(E) + kWave * 8;
 }
 
 hipError_t launch_grouped_gemm_swiglu(const uint16_t* x, const int32_t* offsets, int E,
@@ -413,8 +455,10 @@ hipError_t launch_grouped_gemm_swiglu(const uint16_t* x, const int32_t* offsets,
   hipLaunchKernelGGL(k_gemm_sched, dim3(1), dim3(kSchedThreads), 0, st, offsets, E, N_cap, w);
   if (N_cap == 0) return hipGetLastError();
   const int G = persistent_grid();
-  hipLaunchKernelGGL(k_gemm<0>, dim3(G), dim3(kThreads), 0, st, x, H, wg, wu, I, w, E, h);
-  hipLaunchKernelGGL(k_gemm<1>, dim3(G), dim3(kThreads), 0, st, h, I, wd, nullptr, H, w, E, y);
+  uint2* trash = reinterpret_cast<uint2*>(static_cast<char*>(ws) + trash_offset(E));
+  hipLaunchKernelGGL(k_gemm<0>, dim3(G), dim3(kThreads), 0, st, x, H, wg, wu, I, w, E, h, trash);
+  hipLaunchKernelGGL(k_gemm<1>, dim3(G), dim3(kThreads), 0, st, h, I, wd, nullptr, H, w, E, y,
+                     trash);
   return hipGetLastError();
 }
 

@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--op-iters", type=int, default=20)
     ap.add_argument("--no-ops", action="store_true", help="skip the per-workload op table")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=1536)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=6144)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="N",
                     help="only run N device copies of 256 MiB (counter calibration) and exit")
     return ap.parse_args()
@@ -129,6 +129,27 @@ def reorder_bytes(N, H):
 
 def gemm_flops(N, H, I):
     return 6 * N * H * I
+
+
+def gemm_bytes(N, H, I, active_experts):
+    """x read, h written and read back, y written, and the gate/up/down weights
+    of every expert that owns at least one row (each counted once)."""
+    return 2 * (N * H + 2 * N * I + N * H) + active_experts * 3 * H * I * 2
+
+
+def gemm_traffic_record():
+    """HBM bytes per grouped-GEMM call measured by rocprofv3 counters, if the
+    kernel source is unchanged since they were taken (else None)."""
+    import hashlib
+    rec_path = os.path.join(ROOT, "profiles", "gemm_traffic_skewed_layer.json")
+    try:
+        rec = json.load(open(rec_path))
+        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+    except (OSError, ValueError, KeyError):
+        return None
+    if hashlib.sha256(src).hexdigest() != rec.get("source_sha256"):
+        return None
+    return rec
 
 
 # ----------------------------------------------------------------------------- the layer step
@@ -356,10 +377,15 @@ def main():
         f"combine {seg_med[2]:.1f} us, grad {seg_med[3]:.1f} us")
     g_us = float(np.mean(seg[:, 1]))
     g_tf = gemm_flops(n_rows, H, I) / (g_us * 1e-6) / 1e12
+    active = int((d["counts"] > 0).sum().item())
+    rec = gemm_traffic_record()
     roofline = {"bound": "mfma", "kernel": "moe_grouped_gemm_swiglu (sched + gate/up + down)",
                 "achieved": round(g_tf, 1), "peak": BF16_DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(g_tf / BF16_DENSE_PEAK_TFLOPS, 4), "traffic": None,
-                "avg_us": round(g_us, 2), "flops_per_launch": gemm_flops(n_rows, H, I)}
+                "frac": round(g_tf / BF16_DENSE_PEAK_TFLOPS, 4),
+                "traffic": rec["traffic_bytes"] if rec else None,
+                "avg_us": round(g_us, 2), "flops_per_launch": gemm_flops(n_rows, H, I),
+                "algorithmic_bytes_per_launch": gemm_bytes(n_rows, H, I, active),
+                "hbm_gbs_algorithmic": round(gemm_bytes(n_rows, H, I, active) / (g_us * 1e-6) / 1e9, 1)}
     layer_ops = [
         dict(workload=c["name"], **op_entry("permute", float(np.median(seg[:, 0])),
                                             float(np.min(seg[:, 0])),

@@ -7,11 +7,12 @@
 // and 参数说明 (the shared expert carries no weight), with the gather of the
 // expert_parallel.py coverage page (_unpermute).
 //
-// One wave per token. The slot metadata of the token (kind, row, probability,
-// const index) is read once into registers; then each lane walks 16-byte
-// chunks of the hidden dim, issues the K row loads of a chunk back to back and
-// accumulates them in fp32 in slot order, adds the shared row, rounds once
-// to bf16 and stores.
+// One wave per token. Lane k gathers slot k's metadata (kind, row through the
+// optional row map, probability, const index and coefficients) with vector
+// loads; the values are broadcast to the wave with readlane. Each lane then
+// walks 16-byte chunks of the hidden dim, issues the K row loads of a chunk
+// back to back (non-temporal: every row is read once), accumulates them in
+// fp32 in slot order, adds the shared row, rounds once to bf16 and stores.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -22,7 +23,10 @@ constexpr int kWaves = 4;
 
 enum SlotKind : int { kDrop = 0, kRow = 1, kCopy = 2, kConst = 3 };
 
-template <bool kHasRowMap>
+// kAlphaPerH: the const-expert coefficients vary along h (stride_h != 0);
+// otherwise they are one pair per (token, const expert), read with the slot
+// metadata.
+template <bool kHasRowMap, bool kAlphaPerH>
 __global__ void __launch_bounds__(kWaves * kWave)
 k_combine(const uint16_t* __restrict__ expert_out, int64_t N, const int32_t* __restrict__ row_of_slot,
           const int32_t* __restrict__ row_map, const int32_t* __restrict__ ids,
@@ -35,36 +39,48 @@ k_combine(const uint16_t* __restrict__ expert_out, int64_t N, const int32_t* __r
   const int64_t const_lo = copy_lo + sp.num_copy;
   const int64_t id_hi = const_lo + sp.num_const;
 
-  int kind[16];
-  int64_t src[16];  // row offset (elements) for kRow, const index for kConst
-  float p[16];
-#pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    kind[k] = kDrop;
-    src[k] = 0;
-    p[k] = 0.f;
-    if (k < K) {
-      const int64_t s = t * K + k;
-      const int id = ids[s];
-      p[k] = probs[s];
-      if (id >= 0 && id < E) {
-        int64_t row = row_of_slot[s];
-        if (kHasRowMap && row >= 0 && row < N) row = row_map[row];
-        if (row >= 0 && row < N) {
-          kind[k] = kRow;
-          src[k] = row * H;
-        }
-      } else if (id >= copy_lo && id < const_lo) {
-        kind[k] = kCopy;
-      } else if (id >= const_lo && id < id_hi) {
-        kind[k] = kConst;
-        src[k] = id - const_lo;
+  // Slot metadata, lane k for slot k: one vector load per field (and one more
+  // for the row map) instead of a chain of per-slot scalar loads.
+  int m_kind = kDrop, m_src = 0;
+  float m_p = 0.f, m_a1 = 0.f, m_a2 = 0.f;
+  if (lane < K) {
+    const int64_t s = t * K + lane;
+    const int id = ids[s];
+    m_p = probs[s];
+    if (id >= 0 && id < E) {
+      int64_t row = row_of_slot[s];
+      if (kHasRowMap && row >= 0 && row < N) row = row_map[row];
+      if (row >= 0 && row < N) {
+        m_kind = kRow;
+        m_src = static_cast<int>(row);
+      }
+    } else if (id >= copy_lo && id < const_lo) {
+      m_kind = kCopy;
+    } else if (id >= const_lo && id < id_hi) {
+      m_kind = kConst;
+      m_src = static_cast<int>(id - const_lo);
+      if (!kAlphaPerH) {
+        const int64_t ai = t * sp.a_st + int64_t(m_src) * sp.a_sc;
+        m_a1 = sp.alpha1[ai];
+        m_a2 = sp.alpha2[ai];
       }
     }
   }
+  int kind[16], src[16];
+  float p[16], a1[16], a2[16];
+  bool need_ori = false;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    kind[k] = k < K ? __builtin_amdgcn_readlane(m_kind, k) : kDrop;
+    src[k] = __builtin_amdgcn_readlane(m_src, k);
+    p[k] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m_p), k));
+    a1[k] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m_a1), k));
+    a2[k] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m_a2), k));
+    need_ori |= kind[k] == kCopy || kind[k] == kConst;
+  }
 
   const int chunks = H / 8;
-  const uint16_t* orow = sp.ori_x ? sp.ori_x + t * H : nullptr;
+  const uint16_t* orow = need_ori ? sp.ori_x + t * H : nullptr;
   for (int c = lane; c < chunks; c += kWave) {
     const int h0 = c * 8;
     float acc[8];
@@ -74,7 +90,9 @@ k_combine(const uint16_t* __restrict__ expert_out, int64_t N, const int32_t* __r
     Vec8 v[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k)
-      if (kind[k] == kRow) v[k] = load16(expert_out + src[k] + h0);
+      if (kind[k] == kRow) v[k] = load16_nt(expert_out + int64_t(src[k]) * H + h0);
+    float o[8];
+    if (need_ori) unpack8(load16(orow + h0), o);
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       if (kind[k] == kRow) {
@@ -83,30 +101,35 @@ k_combine(const uint16_t* __restrict__ expert_out, int64_t N, const int32_t* __r
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(p[k], f[i], acc[i]);
       } else if (kind[k] == kCopy) {
-        float f[8];
-        unpack8(load16(orow + h0), f);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(p[k], f[i], acc[i]);
+        for (int i = 0; i < 8; ++i) acc[i] = __builtin_fmaf(p[k], o[i], acc[i]);
       } else if (kind[k] == kConst) {
-        float o[8], cv[8];
-        unpack8(load16(orow + h0), o);
-        unpack8(load16(sp.const_v + src[k] * H + h0), cv);
-        const int64_t abase = t * sp.a_st + src[k] * sp.a_sc;
+        float cv[8];
+        unpack8(load16(sp.const_v + int64_t(src[k]) * H + h0), cv);
+        if (kAlphaPerH) {
+          const int64_t abase = t * sp.a_st + int64_t(src[k]) * sp.a_sc;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int64_t ai = abase + int64_t(h0 + i) * sp.a_sh;
-          const float val = sp.alpha1[ai] * o[i] + sp.alpha2[ai] * cv[i];
-          acc[i] = __builtin_fmaf(p[k], val, acc[i]);
+          for (int i = 0; i < 8; ++i) {
+            const int64_t ai = abase + int64_t(h0 + i) * sp.a_sh;
+            const float val = sp.alpha1[ai] * o[i] + sp.alpha2[ai] * cv[i];
+            acc[i] = __builtin_fmaf(p[k], val, acc[i]);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float val = a1[k] * o[i] + a2[k] * cv[i];
+            acc[i] = __builtin_fmaf(p[k], val, acc[i]);
+          }
         }
       }
     }
     if (shared_x != nullptr) {
       float f[8];
-      unpack8(load16(shared_x + t * H + h0), f);
+      unpack8(load16_nt(shared_x + t * H + h0), f);
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] += f[i];
     }
-    store16(out + t * H + h0, pack8(acc));
+    store16_nt(out + t * H + h0, pack8(acc));
   }
 }
 
@@ -118,12 +141,17 @@ hipError_t launch_combine(const uint16_t* expert_out, int64_t N, const int32_t* 
                           const uint16_t* shared_x, uint16_t* out, hipStream_t st) {
   if (T == 0) return hipGetLastError();
   const dim3 grid(static_cast<unsigned>(ceil_div(T, kWaves)));
-  if (row_map != nullptr)
-    hipLaunchKernelGGL(k_combine<true>, grid, dim3(kWaves * kWave), 0, st, expert_out, N,
-                       row_of_slot, row_map, ids, probs, T, K, H, E, sp, shared_x, out);
-  else
-    hipLaunchKernelGGL(k_combine<false>, grid, dim3(kWaves * kWave), 0, st, expert_out, N,
-                       row_of_slot, row_map, ids, probs, T, K, H, E, sp, shared_x, out);
+  const dim3 block(kWaves * kWave);
+  const bool per_h = sp.num_const > 0 && sp.a_sh != 0;
+#define MOE_COMBINE(RM, PH)                                                                    \
+  hipLaunchKernelGGL((k_combine<RM, PH>), grid, block, 0, st, expert_out, N, row_of_slot,     \
+                     row_map, ids, probs, T, K, H, E, sp, shared_x, out)
+  if (row_map != nullptr) {
+    if (per_h) MOE_COMBINE(true, true); else MOE_COMBINE(true, false);
+  } else {
+    if (per_h) MOE_COMBINE(false, true); else MOE_COMBINE(false, false);
+  }
+#undef MOE_COMBINE
   return hipGetLastError();
 }
 

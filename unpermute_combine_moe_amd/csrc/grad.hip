@@ -51,7 +51,7 @@ k_unpermute_grad(const uint16_t* __restrict__ grad_out, const uint16_t* __restri
 #pragma unroll
     for (int j = 0; j < kCpl; ++j) {
       const int c = lane + j * kWave;
-      if (c < chunks) pv[j] = load16(prow + c * 8);
+      if (c < chunks) pv[j] = load16_nt(prow + c * 8);
     }
     float dot = 0.f;
 #pragma unroll

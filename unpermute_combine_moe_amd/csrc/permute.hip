@@ -9,9 +9,11 @@
 // Layout of the work: the T*K slots are cut into chunks of kChunkWaves waves x
 // 64 lanes x `iters` slots; wave w of a chunk owns a contiguous run of
 // 64*iters slots, so "earlier wave" means "earlier slots". Counts are kept per
-// (expert, chunk) in an expert-major table; its exclusive scan gives every
-// chunk its first row inside every bucket. No global atomics: rank assignment
-// is deterministic.
+// (expert, chunk); a chunk's first row inside bucket e is the offset of e plus
+// the counts of e in earlier chunks. The chunk size keeps the count table
+// small, so every scatter workgroup derives these from the whole table itself
+// (two launches before the row copy). No global atomics: rank assignment is
+// deterministic.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -20,7 +22,6 @@ namespace {
 
 constexpr int kChunkWaves = 4;
 constexpr int kChunkThreads = kChunkWaves * kWave;
-constexpr int kScanThreads = 1024;
 
 struct PermutePlan {
   int iters;    // slots per lane per chunk
@@ -28,10 +29,18 @@ struct PermutePlan {
   int64_t nblk; // number of chunks
 };
 
-PermutePlan plan_for(int64_t S) {
+// Chunks are sized so the (chunk, expert) count table holds at most
+// kTableMax entries (every scatter workgroup reads all of it), with at least
+// kMinIters slots per lane: more, smaller chunks lengthen the table walk more
+// than they shorten the scatter.
+constexpr int64_t kTableMax = 16384;
+constexpr int kMinIters = 8;
+
+PermutePlan plan_for(int64_t S, int E) {
   PermutePlan p;
-  // at least 8 slots per lane; at most 1024 chunks so the scan table stays small
-  p.iters = static_cast<int>(std::max<int64_t>(8, ceil_div(S, int64_t(kChunkThreads) * 1024)));
+  const int64_t target = std::max<int64_t>(1, std::min<int64_t>(256, kTableMax / E));
+  p.iters = static_cast<int>(
+      std::max<int64_t>(kMinIters, ceil_div(S, int64_t(kChunkThreads) * target)));
   p.chunk = int64_t(kChunkThreads) * p.iters;
   p.nblk = ceil_div(S, p.chunk);
   return p;
@@ -48,10 +57,10 @@ __device__ __forceinline__ uint64_t match_key(int key, int nbits) {
   return m;
 }
 
-// Per-chunk histogram: blk_hist[e * nblk + b] = #slots of chunk b with id e.
+// Per-chunk histogram, chunk-major: hist[b * E + e] = #slots of chunk b with id e.
 __global__ void __launch_bounds__(kChunkThreads)
-k_route_count(const int32_t* __restrict__ ids, int64_t S, int E, int iters, int64_t nblk,
-              int32_t* __restrict__ blk_hist) {
+k_route_count(const int32_t* __restrict__ ids, int64_t S, int E, int iters,
+              int32_t* __restrict__ hist) {
   extern __shared__ int32_t cnt[];  // [E]
   for (int e = threadIdx.x; e < E; e += kChunkThreads) cnt[e] = 0;
   __syncthreads();
@@ -65,65 +74,20 @@ k_route_count(const int32_t* __restrict__ ids, int64_t S, int E, int iters, int6
     }
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kChunkThreads) blk_hist[int64_t(e) * nblk + b] = cnt[e];
+  for (int e = threadIdx.x; e < E; e += kChunkThreads) hist[b * E + e] = cnt[e];
 }
 
-// Exclusive scan of the expert-major (expert, chunk) table, in place, by one
-// workgroup; also writes the per-expert counts and offsets.
-__global__ void __launch_bounds__(kScanThreads)
-k_route_scan(int32_t* __restrict__ table, int E, int64_t nblk, int32_t* __restrict__ counts,
-             int32_t* __restrict__ offsets) {
-  __shared__ int32_t part[kScanThreads];
-  __shared__ int32_t total_s;
-  const int64_t L = int64_t(E) * nblk;
-  const int64_t seg = ceil_div(L, kScanThreads);
-  const int64_t lo = std::min<int64_t>(L, threadIdx.x * seg);
-  const int64_t hi = std::min<int64_t>(L, lo + seg);
-  int32_t sum = 0;
-  for (int64_t i = lo; i < hi; ++i) sum += table[i];
-  part[threadIdx.x] = sum;
-  __syncthreads();
-  // Hillis-Steele inclusive scan of the 1024 partial sums
-  for (int off = 1; off < kScanThreads; off <<= 1) {
-    const int32_t v = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
-    __syncthreads();
-    part[threadIdx.x] += v;
-    __syncthreads();
-  }
-  int32_t run = part[threadIdx.x] - sum;  // exclusive
-  if (threadIdx.x == kScanThreads - 1) total_s = part[threadIdx.x];
-  for (int64_t i = lo; i < hi; ++i) {
-    const int32_t c = table[i];
-    table[i] = run;
-    run += c;
-  }
-  __syncthreads();
-  const int32_t total = total_s;
-  for (int e = threadIdx.x; e < E; e += kScanThreads) {
-    if (nblk == 0) {
-      offsets[e] = 0;
-      counts[e] = 0;
-    } else {
-      const int32_t start = table[int64_t(e) * nblk];
-      const int32_t end = (e + 1 < E) ? table[int64_t(e + 1) * nblk] : total;
-      offsets[e] = start;
-      counts[e] = end - start;
-    }
-  }
-  if (threadIdx.x == 0) offsets[E] = total;
-}
-
-// Stable scatter of slot indices: row_of_slot[s] and sorted_slot[row].
-__global__ void __launch_bounds__(kChunkThreads)
-k_route_scatter(const int32_t* __restrict__ ids, int64_t S, int E, int iters, int64_t nblk,
-                const int32_t* __restrict__ blk_base, const int32_t* __restrict__ offsets,
-                int32_t* __restrict__ sorted_slot, int32_t* __restrict__ row_of_slot) {
-  extern __shared__ int32_t run[];  // [kChunkWaves][E]
+// Stable scatter of the slots of chunk b, given chunk_base(e) = the first row
+// of bucket e that belongs to this chunk: writes row_of_slot[s] and
+// sorted_slot[row], and -1 into sorted_slot rows [N, S) of the chunk's range.
+template <typename ChunkBase>
+__device__ void scatter_chunk(const int32_t* __restrict__ ids, int64_t S, int E, int iters,
+                              int64_t b, ChunkBase chunk_base, int32_t N, int32_t* run,
+                              int32_t* __restrict__ sorted_slot, int32_t* __restrict__ row_of_slot) {
   const int w = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
   for (int i = threadIdx.x; i < kChunkWaves * E; i += kChunkThreads) run[i] = 0;
   __syncthreads();
-  const int64_t b = blockIdx.x;
   const int64_t wbase = b * int64_t(kChunkThreads) * iters + int64_t(w) * kWave * iters;
   int32_t* my = run + w * E;
   // pass 1: per-wave counts
@@ -137,7 +101,7 @@ k_route_scatter(const int32_t* __restrict__ ids, int64_t S, int E, int iters, in
   __syncthreads();
   // first row of every (wave, expert): chunk base plus the counts of earlier waves
   for (int e = threadIdx.x; e < E; e += kChunkThreads) {
-    int32_t r = blk_base[int64_t(e) * nblk + b];
+    int32_t r = chunk_base(e);
 #pragma unroll
     for (int ww = 0; ww < kChunkWaves; ++ww) {
       const int32_t c = run[ww * E + e];
@@ -165,11 +129,75 @@ k_route_scatter(const int32_t* __restrict__ ids, int64_t S, int E, int iters, in
     }
   }
   // rows past N (no slot maps there) read -1
-  const int32_t N = offsets[E];
   const int64_t r_lo = b * int64_t(kChunkThreads) * iters;
   const int64_t r_hi = std::min<int64_t>(S, r_lo + int64_t(kChunkThreads) * iters);
   for (int64_t r = r_lo + threadIdx.x; r < r_hi; r += kChunkThreads)
     if (r >= N) sorted_slot[r] = -1;
+}
+
+// Scan and scatter in one launch: every workgroup sums the chunk-major count
+// table itself (per expert: all chunks, and the chunks before its own), scans
+// the expert totals in LDS, and chunk 0 publishes counts and offsets.
+__global__ void __launch_bounds__(kChunkThreads)
+k_route_scan_scatter(const int32_t* __restrict__ ids, int64_t S, int E, int iters, int64_t nblk,
+                     const int32_t* __restrict__ hist, int32_t* __restrict__ counts,
+                     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_slot,
+                     int32_t* __restrict__ row_of_slot) {
+  extern __shared__ int32_t sm[];  // run[kChunkWaves * E] | before[E] | off[E] | part[kChunkThreads]
+  int32_t* run = sm;
+  int32_t* before = sm + kChunkWaves * E;
+  int32_t* off = before + E;
+  int32_t* part = off + E;
+  const int64_t b = blockIdx.x;
+  for (int e = threadIdx.x; e < E; e += kChunkThreads) {
+    int32_t tot = 0, pre = 0;
+    for (int64_t bb = 0; bb < nblk; ++bb) {
+      const int32_t c = hist[bb * E + e];
+      tot += c;
+      pre += (bb < b) ? c : 0;
+    }
+    off[e] = tot;
+    before[e] = pre;
+  }
+  __syncthreads();
+  // exclusive scan of the expert totals: each thread a contiguous run of experts
+  const int per = (E + kChunkThreads - 1) / kChunkThreads;
+  const int lo = std::min(E, static_cast<int>(threadIdx.x) * per);
+  const int hi = std::min(E, lo + per);
+  int32_t sum = 0;
+  for (int e = lo; e < hi; ++e) sum += off[e];
+  part[threadIdx.x] = sum;
+  __syncthreads();
+  for (int o = 1; o < kChunkThreads; o <<= 1) {
+    const int32_t v = threadIdx.x >= o ? part[threadIdx.x - o] : 0;
+    __syncthreads();
+    part[threadIdx.x] += v;
+    __syncthreads();
+  }
+  int32_t acc = part[threadIdx.x] - sum;
+  const int32_t N = part[kChunkThreads - 1];
+  for (int e = lo; e < hi; ++e) {
+    const int32_t c = off[e];
+    off[e] = acc;
+    if (b == 0) {
+      counts[e] = c;
+      offsets[e] = acc;
+    }
+    acc += c;
+  }
+  if (b == 0 && threadIdx.x == 0) offsets[E] = N;
+  __syncthreads();
+  scatter_chunk(
+      ids, S, E, iters, b, [&](int e) { return off[e] + before[e]; }, N, run, sorted_slot,
+      row_of_slot);
+}
+
+__global__ void __launch_bounds__(kChunkThreads)
+k_route_empty(int E, int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
+  for (int e = threadIdx.x; e <= E; e += kChunkThreads) {
+    if (e < E) counts[e] = 0;
+    offsets[e] = 0;
+  }
 }
 
 // Row copy, token-major: each wave reads its token's row once and writes it to
@@ -187,7 +215,7 @@ k_permute_rows(const uint16_t* __restrict__ x, const int32_t* __restrict__ row_o
   const int chunks = H / 8;
   const uint16_t* src = x + t * H;
   for (int c = lane; c < chunks; c += kWave) {
-    const Vec8 v = load16(src + c * 8);
+    const Vec8 v = load16_nt(src + c * 8);
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       if (k < K && rows[k] >= 0 && rows[k] < S) store16(permuted + int64_t(rows[k]) * H + c * 8, v);
@@ -198,7 +226,7 @@ k_permute_rows(const uint16_t* __restrict__ x, const int32_t* __restrict__ row_o
 }  // namespace
 
 size_t permute_workspace_bytes(int64_t T, int K, int E) {
-  const PermutePlan p = plan_for(T * K);
+  const PermutePlan p = plan_for(T * K, E);
   return static_cast<size_t>(std::max<int64_t>(1, p.nblk) * E) * sizeof(int32_t);
 }
 
@@ -206,22 +234,21 @@ hipError_t launch_permute(const uint16_t* x, const int32_t* ids, int64_t T, int 
                           uint16_t* permuted, int32_t* sorted_slot, int32_t* row_of_slot,
                           int32_t* counts, int32_t* offsets, void* ws, hipStream_t st) {
   const int64_t S = T * K;
-  const PermutePlan p = plan_for(S);
+  const PermutePlan p = plan_for(S, E);
   int32_t* table = static_cast<int32_t*>(ws);
-  if (p.nblk > 0) {
-    hipLaunchKernelGGL(k_route_count, dim3(static_cast<unsigned>(p.nblk)), dim3(kChunkThreads),
-                       E * sizeof(int32_t), st, ids, S, E, p.iters, p.nblk, table);
+  if (p.nblk == 0) {  // no slots: zero counts and offsets
+    hipLaunchKernelGGL(k_route_empty, dim3(1), dim3(kChunkThreads), 0, st, E, counts, offsets);
+    return hipGetLastError();
   }
-  hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(kScanThreads), 0, st, table, E, p.nblk, counts,
-                     offsets);
-  if (p.nblk > 0) {
-    hipLaunchKernelGGL(k_route_scatter, dim3(static_cast<unsigned>(p.nblk)), dim3(kChunkThreads),
-                       kChunkWaves * E * sizeof(int32_t), st, ids, S, E, p.iters, p.nblk, table,
-                       offsets, sorted_slot, row_of_slot);
-    if (permuted != nullptr) {
-      hipLaunchKernelGGL(k_permute_rows, dim3(static_cast<unsigned>(ceil_div(T, kRowWaves))),
-                         dim3(kRowWaves * kWave), 0, st, x, row_of_slot, T, H, K, S, permuted);
-    }
+  hipLaunchKernelGGL(k_route_count, dim3(static_cast<unsigned>(p.nblk)), dim3(kChunkThreads),
+                     E * sizeof(int32_t), st, ids, S, E, p.iters, table);
+  const size_t lds = (size_t(kChunkWaves) * E + 2 * E + kChunkThreads) * sizeof(int32_t);
+  hipLaunchKernelGGL(k_route_scan_scatter, dim3(static_cast<unsigned>(p.nblk)),
+                     dim3(kChunkThreads), lds, st, ids, S, E, p.iters, p.nblk, table, counts,
+                     offsets, sorted_slot, row_of_slot);
+  if (permuted != nullptr) {
+    hipLaunchKernelGGL(k_permute_rows, dim3(static_cast<unsigned>(ceil_div(T, kRowWaves))),
+                       dim3(kRowWaves * kWave), 0, st, x, row_of_slot, T, H, K, S, permuted);
   }
   return hipGetLastError();
 }

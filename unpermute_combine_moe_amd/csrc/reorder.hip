@@ -132,7 +132,7 @@ k_reorder_rows(const uint16_t* __restrict__ x, const int32_t* __restrict__ ws, i
     if (i >= N || src < 0) continue;
     const uint16_t* s = x + int64_t(src) * H;
     uint16_t* d = y + i * H;
-    for (int c = lane; c < chunks; c += kWave) store16(d + c * 8, load16(s + c * 8));
+    for (int c = lane; c < chunks; c += kWave) store16_nt(d + c * 8, load16_nt(s + c * 8));
   }
 }
 

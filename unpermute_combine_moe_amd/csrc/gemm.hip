@@ -32,7 +32,7 @@
 // of 16 lanes, output lane 4a+b takes element b of input lanes a, a+4, a+8,
 // a+12, so input lane i points at row k0 + i/4, column 4*(i%4).
 // Both tiles are stored in 16-byte chunks with an XOR swizzle of the chunk
-// index (A: by row & 7, B: by 4 * (k & 3)) that keeps the operand reads free of
+// index (A: by (row / 2) & 7, B: by 4 * (k & 3)) that keeps the operand reads free of
 // bank conflicts; the swizzle is applied by choosing which global chunk each
 // lane loads, since a direct-to-LDS load writes lane L at base + 16 L.
 #include "common.hpp"
@@ -54,7 +54,9 @@ constexpr int kSchedThreads = 1024;
 constexpr int kMaxExperts = 1024;
 constexpr int kXcds = 8;
 
-__device__ __forceinline__ int swz(int row, int kc) { return row * (BK / 8) + (kc ^ (row & 7)); }
+// (the row term (row / 2) & 7 spreads any 16 consecutive rows of 128 bytes
+// over all 16 bank groups of 16 bytes)
+__device__ __forceinline__ int swz(int row, int kc) { return row * (BK / 8) + (kc ^ ((row >> 1) & 7)); }
 
 // ws layout (int32): tile_prefix[E+1] | offs[E+1]
 __global__ void __launch_bounds__(kSchedThreads)
@@ -245,7 +247,7 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
     for (int i = 0; i < kLoadsA; ++i) {
       const int slot = i * kThreads + wave * kWave + lane;
       const int m = slot >> 3;
-      const int kc = (slot & 7) ^ (m & 7);
+      const int kc = (slot & 7) ^ ((m >> 1) & 7);
       const int r = std::min(t.row0 + m, t.row_end - 1);
       a_src[i] = A + int64_t(r) * Kdim + kc * 8;
     }

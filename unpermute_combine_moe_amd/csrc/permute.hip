@@ -57,6 +57,10 @@ __device__ __forceinline__ uint64_t match_key(int key, int nbits) {
   return m;
 }
 
+// Ids are read in batches of kBatch per lane: the loads of a batch are
+// independent, so a batch costs one memory latency instead of kBatch.
+constexpr int kBatch = 8;
+
 // Per-chunk histogram, chunk-major: hist[b * E + e] = #slots of chunk b with id e.
 __global__ void __launch_bounds__(kChunkThreads)
 k_route_count(const int32_t* __restrict__ ids, int64_t S, int E, int iters,
@@ -66,12 +70,16 @@ k_route_count(const int32_t* __restrict__ ids, int64_t S, int E, int iters,
   __syncthreads();
   const int64_t b = blockIdx.x;
   const int64_t base = b * int64_t(kChunkThreads) * iters;
-  for (int j = 0; j < iters; ++j) {
-    const int64_t s = base + int64_t(j) * kChunkThreads + threadIdx.x;
-    if (s < S) {
-      const int id = ids[s];
-      if (id >= 0 && id < E) atomicAdd(&cnt[id], 1);
+  for (int j0 = 0; j0 < iters; j0 += kBatch) {
+    int id[kBatch];
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      const int64_t s = base + int64_t(j0 + q) * kChunkThreads + threadIdx.x;
+      id[q] = (j0 + q < iters && s < S) ? ids[s] : -1;
     }
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q)
+      if (id[q] >= 0 && id[q] < E) atomicAdd(&cnt[id[q]], 1);
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += kChunkThreads) hist[b * E + e] = cnt[e];
@@ -90,13 +98,21 @@ __device__ void scatter_chunk(const int32_t* __restrict__ ids, int64_t S, int E,
   __syncthreads();
   const int64_t wbase = b * int64_t(kChunkThreads) * iters + int64_t(w) * kWave * iters;
   int32_t* my = run + w * E;
-  // pass 1: per-wave counts
-  for (int j = 0; j < iters; ++j) {
-    const int64_t s = wbase + int64_t(j) * kWave + lane;
-    if (s < S) {
-      const int id = ids[s];
-      if (id >= 0 && id < E) atomicAdd(&my[id], 1);
+  // ids of slots wbase + (j0 + q) * 64 + lane, q < kBatch
+  auto load_batch = [&](int j0, int id[kBatch]) {
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      const int64_t s = wbase + int64_t(j0 + q) * kWave + lane;
+      id[q] = (j0 + q < iters && s < S) ? ids[s] : -1;
     }
+  };
+  // pass 1: per-wave counts
+  for (int j0 = 0; j0 < iters; j0 += kBatch) {
+    int id[kBatch];
+    load_batch(j0, id);
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q)
+      if (id[q] >= 0 && id[q] < E) atomicAdd(&my[id[q]], 1);
   }
   __syncthreads();
   // first row of every (wave, expert): chunk base plus the counts of earlier waves
@@ -113,19 +129,24 @@ __device__ void scatter_chunk(const int32_t* __restrict__ ids, int64_t S, int E,
   // pass 2: each wave walks its slots in order; lanes with equal ids are ranked
   // by lane index, and the group's lowest lane advances the running row.
   const int nbits = 32 - __builtin_clz(static_cast<unsigned>(E));  // keys 0..E fit
-  for (int j = 0; j < iters; ++j) {
-    const int64_t s = wbase + int64_t(j) * kWave + lane;
-    int id = (s < S) ? ids[s] : -1;
-    const bool real = id >= 0 && id < E;
-    const int key = real ? id : E;
-    const uint64_t same = match_key(key, nbits);
-    const int rank = rank_below(same);
-    int32_t row = -1;
-    if (real) row = my[id] + rank;
-    if (real && rank == 0) my[id] += __popcll(same);
-    if (s < S) {
-      row_of_slot[s] = row;
-      if (real) sorted_slot[row] = static_cast<int32_t>(s);
+  for (int j0 = 0; j0 < iters; j0 += kBatch) {
+    int id[kBatch];
+    load_batch(j0, id);
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) {
+      if (j0 + q >= iters) break;
+      const int64_t s = wbase + int64_t(j0 + q) * kWave + lane;
+      const bool real = id[q] >= 0 && id[q] < E;
+      const int key = real ? id[q] : E;
+      const uint64_t same = match_key(key, nbits);
+      const int rank = rank_below(same);
+      int32_t row = -1;
+      if (real) row = my[id[q]] + rank;
+      if (real && rank == 0) my[id[q]] += __popcll(same);
+      if (s < S) {
+        row_of_slot[s] = row;
+        if (real) sorted_slot[row] = static_cast<int32_t>(s);
+      }
     }
   }
   // rows past N (no slot maps there) read -1
@@ -151,10 +172,15 @@ k_route_scan_scatter(const int32_t* __restrict__ ids, int64_t S, int E, int iter
   const int64_t b = blockIdx.x;
   for (int e = threadIdx.x; e < E; e += kChunkThreads) {
     int32_t tot = 0, pre = 0;
-    for (int64_t bb = 0; bb < nblk; ++bb) {
-      const int32_t c = hist[bb * E + e];
-      tot += c;
-      pre += (bb < b) ? c : 0;
+    for (int64_t b0 = 0; b0 < nblk; b0 += kBatch) {
+      int32_t c[kBatch];
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) c[q] = (b0 + q < nblk) ? hist[(b0 + q) * E + e] : 0;
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) {
+        tot += c[q];
+        pre += (b0 + q < b) ? c[q] : 0;
+      }
     }
     off[e] = tot;
     before[e] = pre;

@@ -123,6 +123,10 @@ def grad_bytes(T, K, H, N):
     return T * H * 2 + 2 * N * H * 2 + 2 * T * K * 4 + T * K * 4
 
 
+def permute_grad_bytes(T, K, H, N):
+    return N * H * 2 + T * K * 4 + T * H * 2
+
+
 def reorder_bytes(N, H):
     return 2 * N * H * 2 + 2 * N * 4
 
@@ -304,6 +308,13 @@ def run_ops(args, dev, flush):
     ops.append(dict(workload=c["name"], **op_entry("unpermute_grad",
                                                    *time_op(f_grad, args.op_iters, flush),
                                                    nbytes=grad_bytes(T, K, H, N))))
+    # permute backward on the same routing: the gradient of the permuted rows summed per token
+    dx = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    f_pgrad = lambda: moe.moe_permute_grad(dperm, N, p5["row_of_slot"], T, K, H, dx)
+    ops.append(dict(workload=c["name"], **op_entry("permute_grad",
+                                                   *time_op(f_pgrad, args.op_iters, flush),
+                                                   nbytes=permute_grad_bytes(T, K, H, N))))
+    del dx
     del gout, perm5, dperm
     # device-to-device copy of 1 GiB for reference
     a = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev)

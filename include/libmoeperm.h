@@ -241,6 +241,24 @@ moe_status_t moe_unpermute_grad(const void* grad_out, const void* permuted, int6
                                 int32_t K, int32_t H, void* d_permuted, float* d_probs,
                                 hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * moe_permute_grad -- backward of moe_permute's row copy.
+ *
+ * [GMM] (fix 2 of the PR description): the permute is the advanced-index
+ * gather x[idx], whose backward index_put accumulates the gradients of
+ * repeated indices. Row row_of_slot[t*K + k] holds a copy of x[t], so
+ *     d_x[t] = bf16( sum_k d_permuted[row_of_slot[t*K + k]] )   (fp32 accumulate, k order)
+ * over the slots whose row is in [0, N); a token without such a slot gets 0.
+ * (The combine with every weight 1 and no special or shared term.)
+ *
+ *  d_permuted  bf16 [N, H]   in (may be NULL iff N == 0)
+ *  row_of_slot int32 [T*K]   in      d_x  bf16 [T, H]  out
+ * Errors: INVALID_ARG for T < 0, K outside [1,16], H <= 0, N < 0, T*K or N >
+ * INT32_MAX, NULL / misaligned pointers; UNSUPPORTED for H % 8 != 0.
+ * ------------------------------------------------------------------------ */
+moe_status_t moe_permute_grad(const void* d_permuted, int64_t N, const int32_t* row_of_slot,
+                              int64_t T, int32_t K, int32_t H, void* d_x, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -50,6 +50,7 @@ def _load():
                                 _u16p, _u16p, _f64p]
     lib.orc_unpermute_grad.argtypes = [_u16p, _u16p, _i64, _i32p, _f32p, _i64, _i32, _i32, _u16p,
                                        _f32p, _f64p, _f64p]
+    lib.orc_permute_grad.argtypes = [_u16p, _i64, _i32p, _i64, _i32, _i32, _u16p, _f64p]
     lib.orc_num_threads.argtypes = []
     for name in ("orc_permute", "orc_reorder_loop", "orc_reorder_index_vectorized",
                  "orc_swiglu_row", "orc_grouped_swiglu", "orc_combine", "orc_unpermute_grad",
@@ -244,3 +245,18 @@ def unpermute_grad(grad_out, permuted, row_of_slot, probs, *, d_permuted_init=No
                                     _ptr(dprobs64, ctypes.c_double))
     _check(rc, "unpermute_grad")
     return dperm, dprobs, dperm64, dprobs64
+
+
+def permute_grad(d_permuted, row_of_slot):
+    """Permute backward: returns (d_x bf16 [T,H], d_x_f64 [T,H]);
+    d_x[t] = sum over the token's slots with a row of d_permuted[row]."""
+    dp = _c(d_permuted, np.uint16)
+    ros = _c(row_of_slot, np.int32)
+    T, K = ros.shape
+    N, H = dp.shape
+    dx = np.empty((T, H), dtype=np.uint16)
+    dx64 = np.empty((T, H), dtype=np.float64)
+    rc = _load().orc_permute_grad(_ptr(dp, ctypes.c_uint16), N, _ptr(ros, ctypes.c_int32), T, K,
+                                  H, _ptr(dx, ctypes.c_uint16), _ptr(dx64, ctypes.c_double))
+    _check(rc, "permute_grad")
+    return dx, dx64

@@ -196,6 +196,22 @@ def test_grad_checks(lib):
     assert _grad(lib, probs=PM) == INVALID
 
 
+def _pgrad(lib, dperm=P, N=100, ros=P, T=50, K=2, H=64, dx=P):
+    return lib.moe_permute_grad(dperm, N, ros, T, K, H, dx, None)
+
+
+@no_gpu
+def test_permute_grad_checks(lib):
+    assert _pgrad(lib, T=-1) == INVALID
+    assert _pgrad(lib, K=17) == INVALID
+    assert _pgrad(lib, H=12) == UNSUPPORTED
+    assert _pgrad(lib, N=-1) == INVALID
+    assert _pgrad(lib, N=2**31) == INVALID
+    assert _pgrad(lib, dperm=None) == INVALID
+    assert _pgrad(lib, ros=PM) == INVALID
+    assert _pgrad(lib, dx=P + 8) == INVALID
+
+
 def test_binding_rejects_wrong_tensors(lib):
     from unpermute_combine_moe_amd import binding as b
 

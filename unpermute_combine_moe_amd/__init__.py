@@ -1,6 +1,6 @@
 """MI355X-native MoE expert hot path: token permute, rank-major -> expert-major
 reorder, grouped SwiGLU GEMM (bf16 MFMA), weighted unpermute-combine with
-special experts, and the unpermute backward.
+special experts, the unpermute backward and the permute backward.
 
 The computation lives in libmoeperm.so (hand-written HIP for gfx950, C ABI in
 include/libmoeperm.h); this package only binds it. Build it with
@@ -11,5 +11,6 @@ from .binding import (  # noqa: F401
     make_special, moe_grouped_gemm_swiglu, moe_grouped_gemm_swiglu_workspace_size, moe_permute,
     moe_permute_workspace_size, moe_rank_to_expert_reorder,
     moe_rank_to_expert_reorder_workspace_size, moe_unpermute_combine, moe_unpermute_grad,
-    permute_alloc, reorder_alloc, status_str, unpermute_grad_alloc, workspace,
+    moe_permute_grad, permute_alloc, permute_grad_alloc, reorder_alloc, status_str,
+    unpermute_grad_alloc, workspace,
 )

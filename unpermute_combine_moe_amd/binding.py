@@ -46,7 +46,7 @@ EXPORTS = (
     "moe_permute_workspace_size", "moe_permute",
     "moe_rank_to_expert_reorder_workspace_size", "moe_rank_to_expert_reorder",
     "moe_grouped_gemm_swiglu_workspace_size", "moe_grouped_gemm_swiglu",
-    "moe_unpermute_combine", "moe_unpermute_grad",
+    "moe_unpermute_combine", "moe_unpermute_grad", "moe_permute_grad",
 )
 
 _lib = None
@@ -78,6 +78,7 @@ def load(path: str = LIB_PATH):
     lib.moe_unpermute_combine.argtypes = [_vp, _i64, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32,
                                           ctypes.POINTER(MoeSpecialExperts), _vp, _vp, _vp]
     lib.moe_unpermute_grad.argtypes = [_vp, _vp, _i64, _vp, _vp, _i64, _i32, _i32, _vp, _vp, _vp]
+    lib.moe_permute_grad.argtypes = [_vp, _i64, _vp, _i64, _i32, _i32, _vp, _vp]
     for name in EXPORTS[2:]:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -204,6 +205,12 @@ def moe_unpermute_grad(grad_out, permuted, N, row_of_slot, probs, T, K, H, d_per
         "moe_unpermute_grad")
 
 
+def moe_permute_grad(d_permuted, N, row_of_slot, T, K, H, d_x, stream=None):
+    _check(load().moe_permute_grad(
+        _ptr(d_permuted, _BF16, "d_permuted"), N, _ptr(row_of_slot, _I32, "row_of_slot"), T, K, H,
+        _ptr(d_x, _BF16, "d_x"), _stream(stream)), "moe_permute_grad")
+
+
 # --------------------------------------------------------------------------- allocating helpers
 
 def permute_alloc(x, expert_ids, num_experts, *, rows: bool = True, stream=None):
@@ -277,3 +284,11 @@ def unpermute_grad_alloc(grad_out, permuted, row_of_slot, probs, *, d_permuted=N
     moe_unpermute_grad(grad_out, permuted, N, row_of_slot, probs, T, K, H, d_permuted, d_probs,
                        stream)
     return d_permuted, d_probs
+
+
+def permute_grad_alloc(d_permuted, row_of_slot, *, stream=None):
+    T, K = row_of_slot.shape
+    N, H = d_permuted.shape
+    d_x = torch.empty((T, H), dtype=_BF16, device=d_permuted.device)
+    moe_permute_grad(d_permuted, N, row_of_slot, T, K, H, d_x, stream)
+    return d_x

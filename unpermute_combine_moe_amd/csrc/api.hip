@@ -216,6 +216,20 @@ MOE_API moe_status_t moe_unpermute_combine(const void* expert_out, int64_t N,
 
 // --------------------------------------------------------------------------- backward
 
+MOE_API moe_status_t moe_permute_grad(const void* d_permuted, int64_t N,
+                                      const int32_t* row_of_slot, int64_t T, int32_t K, int32_t H,
+                                      void* d_x, hipStream_t stream) {
+  if (moe_status_t s = check_tk(T, K)) return s;
+  if (moe_status_t s = check_h(H)) return s;
+  if (N < 0 || N > INT32_MAX) return MOE_ERR_INVALID_ARG;
+  if (T > 0) {
+    if (!word_ok(row_of_slot) || !row_ok(d_x)) return MOE_ERR_INVALID_ARG;
+    if (N > 0 && !row_ok(d_permuted)) return MOE_ERR_INVALID_ARG;
+  }
+  return hip_status(moe::launch_permute_grad(u16(d_permuted), N, row_of_slot, T, K, H, u16(d_x),
+                                             stream));
+}
+
 MOE_API moe_status_t moe_unpermute_grad(const void* grad_out, const void* permuted, int64_t N,
                                         const int32_t* row_of_slot, const float* probs,
                                         int64_t T, int32_t K, int32_t H, void* d_permuted,

@@ -25,8 +25,9 @@ enum SlotKind : int { kDrop = 0, kRow = 1, kCopy = 2, kConst = 3 };
 
 // kAlphaPerH: the const-expert coefficients vary along h (stride_h != 0);
 // otherwise they are one pair per (token, const expert), read with the slot
-// metadata.
-template <bool kHasRowMap, bool kAlphaPerH>
+// metadata. kUnit: the permute backward -- every slot with a row has weight
+// 1 and there are no ids, special experts or shared term.
+template <bool kHasRowMap, bool kAlphaPerH, bool kUnit = false>
 __global__ void __launch_bounds__(kWaves * kWave)
 k_combine(const uint16_t* __restrict__ expert_out, int64_t N, const int32_t* __restrict__ row_of_slot,
           const int32_t* __restrict__ row_map, const int32_t* __restrict__ ids,
@@ -43,7 +44,14 @@ k_combine(const uint16_t* __restrict__ expert_out, int64_t N, const int32_t* __r
   // for the row map) instead of a chain of per-slot scalar loads.
   int m_kind = kDrop, m_src = 0;
   float m_p = 0.f, m_a1 = 0.f, m_a2 = 0.f;
-  if (lane < K) {
+  if (kUnit && lane < K) {
+    const int64_t row = row_of_slot[t * K + lane];
+    if (row >= 0 && row < N) {
+      m_kind = kRow;
+      m_src = static_cast<int>(row);
+      m_p = 1.0f;
+    }
+  } else if (lane < K) {
     const int64_t s = t * K + lane;
     const int id = ids[s];
     m_p = probs[s];
@@ -152,6 +160,17 @@ hipError_t launch_combine(const uint16_t* expert_out, int64_t N, const int32_t* 
     if (per_h) MOE_COMBINE(false, true); else MOE_COMBINE(false, false);
   }
 #undef MOE_COMBINE
+  return hipGetLastError();
+}
+
+hipError_t launch_permute_grad(const uint16_t* d_permuted, int64_t N, const int32_t* row_of_slot,
+                               int64_t T, int K, int H, uint16_t* d_x, hipStream_t st) {
+  if (T == 0) return hipGetLastError();
+  const dim3 grid(static_cast<unsigned>(ceil_div(T, kWaves)));
+  const dim3 block(kWaves * kWave);
+  hipLaunchKernelGGL((k_combine<false, false, true>), grid, block, 0, st, d_permuted, N,
+                     row_of_slot, nullptr, nullptr, nullptr, T, K, H, 0, SpecialArgs{}, nullptr,
+                     d_x);
   return hipGetLastError();
 }
 

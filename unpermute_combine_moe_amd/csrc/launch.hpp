@@ -32,6 +32,9 @@ hipError_t launch_combine(const uint16_t* expert_out, int64_t N, const int32_t* 
                           int64_t T, int K, int H, int E, const SpecialArgs& sp,
                           const uint16_t* shared_x, uint16_t* out, hipStream_t st);
 
+hipError_t launch_permute_grad(const uint16_t* d_permuted, int64_t N, const int32_t* row_of_slot,
+                               int64_t T, int K, int H, uint16_t* d_x, hipStream_t st);
+
 hipError_t launch_unpermute_grad(const uint16_t* grad_out, const uint16_t* permuted, int64_t N,
                                  const int32_t* row_of_slot, const float* probs, int64_t T, int K,
                                  int H, uint16_t* d_permuted, float* d_probs, hipStream_t st);

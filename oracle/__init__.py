@@ -18,6 +18,7 @@ _lib = None
 _i32p = ctypes.POINTER(ctypes.c_int32)
 _u16p = ctypes.POINTER(ctypes.c_uint16)
 _f32p = ctypes.POINTER(ctypes.c_float)
+_u8p = ctypes.POINTER(ctypes.c_uint8)
 _f64p = ctypes.POINTER(ctypes.c_double)
 _i64 = ctypes.c_int64
 _i32 = ctypes.c_int32
@@ -51,10 +52,14 @@ def _load():
     lib.orc_unpermute_grad.argtypes = [_u16p, _u16p, _i64, _i32p, _f32p, _i64, _i32, _i32, _u16p,
                                        _f32p, _f64p, _f64p]
     lib.orc_permute_grad.argtypes = [_u16p, _i64, _i32p, _i64, _i32, _i32, _u16p, _f64p]
+    lib.orc_combine_grad.argtypes = [_u16p, _u16p, _i64, _i32p, _i32p, _i32p, _f32p, _i64, _i32,
+                                     _i32, _i32, _i32, _i32, _i32, _u16p, _f32p, _f32p, _i64,
+                                     _i64, _i64, _i64, _u16p, _f64p, _u8p, _f64p, _f64p, _f64p,
+                                     _f64p, _f64p, _f64p]
     lib.orc_num_threads.argtypes = []
     for name in ("orc_permute", "orc_reorder_loop", "orc_reorder_index_vectorized",
                  "orc_swiglu_row", "orc_grouped_swiglu", "orc_combine", "orc_unpermute_grad",
-                 "orc_num_threads"):
+                 "orc_permute_grad", "orc_combine_grad", "orc_num_threads"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -260,3 +265,42 @@ def permute_grad(d_permuted, row_of_slot):
                                   H, _ptr(dx, ctypes.c_uint16), _ptr(dx64, ctypes.c_double))
     _check(rc, "permute_grad")
     return dx, dx64
+
+
+def combine_grad(grad_out, expert_out, row_of_slot, expert_ids, probs, E: int, *, row_map=None,
+                 num_zero: int = 0, num_copy: int = 0, num_const: int = 0, ori_x=None,
+                 alpha1=None, alpha2=None, alpha_strides=(0, 0, 0), const_v=None):
+    """Backward of combine() (special and shared experts included), all in fp64.
+    Returns a dict: d_expert_out [N,H] (0 in rows no slot references), row_written
+    [N] bool, d_probs [T,K], d_ori_x [T,H], d_alpha1 / d_alpha2 (alpha's flat
+    layout), d_const_v [num_const,H], d_shared [T,H]."""
+    g = _c(grad_out, np.uint16)
+    ids = _c(expert_ids, np.int32)
+    T, K = ids.shape
+    H = g.shape[1]
+    ros = _c(row_of_slot, np.int32)
+    pr = _c(probs, np.float32)
+    eo = _c(expert_out, np.uint16) if expert_out is not None else None
+    N = eo.shape[0] if eo is not None else 0
+    rm = _c(row_map, np.int32) if row_map is not None else None
+    ox = _c(ori_x, np.uint16) if ori_x is not None else None
+    a1 = _c(alpha1, np.float32).reshape(-1) if alpha1 is not None else None
+    a2 = _c(alpha2, np.float32).reshape(-1) if alpha2 is not None else None
+    n_alpha = a1.size if a1 is not None else 0
+    cv = _c(const_v, np.uint16) if const_v is not None else None
+    st, sc, sh = (int(v) for v in alpha_strides)
+    out = dict(d_expert_out=np.zeros((N, H)), row_written=np.zeros(N, np.uint8),
+               d_probs=np.zeros((T, K)), d_ori_x=np.zeros((T, H)), d_alpha1=np.zeros(n_alpha),
+               d_alpha2=np.zeros(n_alpha), d_const_v=np.zeros((num_const, H)),
+               d_shared=np.zeros((T, H)))
+    rc = _load().orc_combine_grad(
+        _ptr(g, ctypes.c_uint16), _ptr(eo, ctypes.c_uint16), N, _ptr(ros, ctypes.c_int32),
+        _ptr(rm, ctypes.c_int32), _ptr(ids, ctypes.c_int32), _ptr(pr, ctypes.c_float), T, K, H, E,
+        num_zero, num_copy, num_const, _ptr(ox, ctypes.c_uint16), _ptr(a1, ctypes.c_float),
+        _ptr(a2, ctypes.c_float), st, sc, sh, n_alpha, _ptr(cv, ctypes.c_uint16),
+        *(_ptr(out[k], ctypes.c_uint8 if k == "row_written" else ctypes.c_double)
+          for k in ("d_expert_out", "row_written", "d_probs", "d_ori_x", "d_alpha1", "d_alpha2",
+                    "d_const_v", "d_shared")))
+    _check(rc, "combine_grad")
+    out["row_written"] = out["row_written"].astype(bool)
+    return out

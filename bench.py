@@ -127,6 +127,15 @@ def permute_grad_bytes(T, K, H, N):
     return N * H * 2 + T * K * 4 + T * H * 2
 
 
+def combine_grad_bytes(T, K, H, N, n_routed, need_ori, num_const):
+    """grad_out read; each routed row read and its gradient written; ori_x read
+    where a copy / const slot needs it; d_ori_x written for every token; the
+    slot metadata, row map and d_probs; const_v read and its gradient written;
+    per-token alpha read and its gradient written."""
+    return (T * H * 2 + 2 * n_routed * H * 2 + need_ori * H * 2 + T * H * 2 + 3 * T * K * 4
+            + N * 4 + T * K * 4 + 2 * num_const * H * 2 + 4 * T * 4)
+
+
 def reorder_bytes(N, H):
     return 2 * N * H * 2 + 2 * N * 4
 
@@ -292,7 +301,22 @@ def run_ops(args, dev, flush):
     ops.append(dict(workload=c["name"], **op_entry(
         "unpermute_combine_special", *time_op(f_comb4, args.op_iters, flush),
         nbytes=n_routed * H * 2 + 4 * T * K * 4 + 2 * T * H * 2 + need_ori * H * 2 + N * 4)))
-    del xr, r, keep, shared, out4
+    # backward of that combine: every input's gradient (special experts included)
+    g4 = dbf(W.normal_bf16(np.random.default_rng(44), (T, H)), dev)
+    d_eo = torch.empty((N, H), dtype=torch.bfloat16, device=dev)
+    d_pr = torch.empty((T, K), dtype=torch.float32, device=dev)
+    d_ori = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    d_a1 = torch.empty(T, dtype=torch.float32, device=dev)
+    d_a2 = torch.empty(T, dtype=torch.float32, device=dev)
+    d_cv = torch.empty((c["num_const"], H), dtype=torch.bfloat16, device=dev)
+    wsg = moe.workspace(moe.moe_unpermute_combine_grad_workspace_size(T, H, c["num_const"]), dev)
+    f_cgrad = lambda: moe.moe_unpermute_combine_grad(g4, r["y"], N, src, r["inv_perm"], ids4,
+                                                     probs4, T, K, H, El, sp, d_eo, d_pr, d_ori,
+                                                     d_a1, d_a2, d_cv, wsg)
+    ops.append(dict(workload=c["name"], **op_entry(
+        "unpermute_combine_grad_special", *time_op(f_cgrad, args.op_iters, flush),
+        nbytes=combine_grad_bytes(T, K, H, N, n_routed, need_ori, c["num_const"]))))
+    del xr, r, keep, shared, out4, g4, d_eo, d_ori
     # unpermute backward, T=16384 H=4096 E=128 K=8
     g = W.gen_c5()
     c = g["cfg"]

@@ -219,6 +219,56 @@ moe_status_t moe_unpermute_combine(const void* expert_out, int64_t N, const int3
                                    const void* shared_x, void* out, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * moe_unpermute_combine_grad -- backward of moe_unpermute_combine, special
+ * and shared experts included.
+ *
+ * [CV2] 计算公式: the combine is out[t] = sum_k p[t,k] v_k(t) + shared[t]
+ * with v_k an expert row, 0 (zero expert), ori_x[t] (copy expert) or
+ * a1*ori_x[t] + a2*const_v[c] (const expert c, a* = alpha*(t, c, h)). Given
+ * g = grad_out, this call returns the gradient of every input of that sum:
+ *     d_expert_out[row] = bf16( p g[t] )       routed slot (row via row_map)
+ *     d_probs[t,k]      = sum_h g[t,h] v_k(t,h)     (0 for zero / dropped slots)
+ *     d_ori_x[t]        = bf16( sum_copy p g[t] + sum_const p a1 g[t] )
+ *     d_alpha1(t,c,h)  += p g ori_x[t,h]     d_alpha2(t,c,h) += p g const_v[c,h]
+ *     d_const_v[c]      = bf16( sum over tokens and slots of p a2 g[t] )
+ * all accumulated in fp32. The shared term is added once with no weight
+ * ([CV2] 参数说明), so its gradient is grad_out itself: there is no output
+ * for it. Rows of d_expert_out that no slot references are not written.
+ *
+ * d_alpha1 / d_alpha2 have alpha's layout (the same strides); every element
+ * alpha reads is written (0 where no slot uses it). Supported layouts for
+ * them: each token owns its span (stride_h = 0, stride_t > 0,
+ * (num_const-1)*stride_c < stride_t: per-token [T] or [T, num_const]), or
+ * all tokens share it (stride_t = 0 with stride_h = 1 and stride_c >= H: the
+ * page's [num_const, H]; or stride_h = 0: [num_const] or one scalar).
+ * Sums over tokens (d_const_v, shared alpha layouts) go through fp32
+ * per-segment partials in the workspace, added in a fixed order: the result
+ * is deterministic.
+ *
+ *  grad_out      bf16 [T, H]   in          (the other inputs as for the combine)
+ *  d_expert_out  bf16 [N, H]   out (nullable: not computed)
+ *  d_probs       fp32 [T*K]    out
+ *  d_ori_x       bf16 [T, H]   out (nullable); zero rows for tokens without
+ *                                  copy / const slots
+ *  d_alpha1, d_alpha2  fp32, alpha's layout   out (nullable)
+ *  d_const_v     bf16 [num_const, H]  out (nullable)
+ *  workspace     moe_unpermute_combine_grad_workspace_size(T, H, num_const)
+ *                bytes, 16-byte aligned; needed only when num_const > 0 and
+ *                d_const_v or a shared-layout d_alpha is requested
+ * Errors: as moe_unpermute_combine, plus NULL grad_out / d_probs and
+ * misaligned outputs (INVALID_ARG); UNSUPPORTED for a d_alpha request with
+ * any other alpha layout; WORKSPACE if the workspace is missing or small.
+ * ------------------------------------------------------------------------ */
+moe_status_t moe_unpermute_combine_grad_workspace_size(int64_t T, int32_t H, int32_t num_const,
+                                                      size_t* bytes);
+moe_status_t moe_unpermute_combine_grad(
+    const void* grad_out, const void* expert_out, int64_t N, const int32_t* row_of_slot,
+    const int32_t* row_map, const int32_t* expert_ids, const float* probs, int64_t T, int32_t K,
+    int32_t H, int32_t num_experts, const moe_special_experts_t* special, void* d_expert_out,
+    float* d_probs, void* d_ori_x, float* d_alpha1, float* d_alpha2, void* d_const_v,
+    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * moe_unpermute_grad -- backward of the routed part of the combine.
  *
  * [UNP] 主要改动: npu_moe_token_unpermute_grad_v2 returns the gradient of

@@ -212,6 +212,40 @@ def test_permute_grad_checks(lib):
     assert _pgrad(lib, dx=P + 8) == INVALID
 
 
+def _cgrad(lib, g=P, eo=P, N=100, ros=P, rmap=None, ids=P, probs=P, T=50, K=2, H=64, E=8,
+           sp=None, deo=P, dpr=P, dori=P, da1=None, da2=None, dcv=None, ws=P, wsb=1 << 24):
+    spp = ctypes.byref(sp) if sp is not None else None
+    return lib.moe_unpermute_combine_grad(g, eo, N, ros, rmap, ids, probs, T, K, H, E, spp, deo,
+                                          dpr, dori, da1, da2, dcv, ws, wsb, None)
+
+
+@no_gpu
+def test_combine_grad_checks(lib):
+    from unpermute_combine_moe_amd.binding import MoeSpecialExperts as S
+    from unpermute_combine_moe_amd import binding as b
+
+    tok = S(0, 1, 2, P, P, P, 1, 0, 0, P)           # per-token alpha
+    other = S(0, 1, 2, P, P, P, 64, 0, 1, P)        # [T, H] alpha: no d_alpha kernel
+    assert _cgrad(lib, T=-1) == INVALID
+    assert _cgrad(lib, K=17) == INVALID
+    assert _cgrad(lib, H=12) == UNSUPPORTED
+    assert _cgrad(lib, g=None) == INVALID
+    assert _cgrad(lib, dpr=None) == INVALID
+    assert _cgrad(lib, deo=P + 2) == INVALID
+    assert _cgrad(lib, dori=P + 8) == INVALID
+    assert _cgrad(lib, sp=tok, da1=P + 2) == INVALID
+    assert _cgrad(lib, sp=S(0, 0, 1, P, None, P, 1, 0, 0, P)) == INVALID     # alpha1 missing
+    assert _cgrad(lib, sp=other, da1=P) == UNSUPPORTED
+    assert _cgrad(lib, sp=tok, dcv=P, ws=None) == WORKSPACE
+    need = b.moe_unpermute_combine_grad_workspace_size(50, 64, 2)
+    assert _cgrad(lib, sp=tok, dcv=P, wsb=need - 1) == WORKSPACE
+    assert _cgrad(lib, sp=tok, dcv=P, ws=P + 4) == WORKSPACE
+    assert b.moe_unpermute_combine_grad_workspace_size(50, 64, 0) > 0
+    assert b.moe_unpermute_combine_grad_workspace_size(8192, 4096, 4) >= 3 * 4 * 4096 * 4
+    with pytest.raises(b.MoeError):
+        b.moe_unpermute_combine_grad_workspace_size(-1, 64, 2)
+
+
 def test_binding_rejects_wrong_tensors(lib):
     from unpermute_combine_moe_amd import binding as b
 

@@ -47,6 +47,7 @@ EXPORTS = (
     "moe_rank_to_expert_reorder_workspace_size", "moe_rank_to_expert_reorder",
     "moe_grouped_gemm_swiglu_workspace_size", "moe_grouped_gemm_swiglu",
     "moe_unpermute_combine", "moe_unpermute_grad", "moe_permute_grad",
+    "moe_unpermute_combine_grad_workspace_size", "moe_unpermute_combine_grad",
 )
 
 _lib = None
@@ -79,6 +80,10 @@ def load(path: str = LIB_PATH):
                                           ctypes.POINTER(MoeSpecialExperts), _vp, _vp, _vp]
     lib.moe_unpermute_grad.argtypes = [_vp, _vp, _i64, _vp, _vp, _i64, _i32, _i32, _vp, _vp, _vp]
     lib.moe_permute_grad.argtypes = [_vp, _i64, _vp, _i64, _i32, _i32, _vp, _vp]
+    lib.moe_unpermute_combine_grad_workspace_size.argtypes = [_i64, _i32, _i32, sz]
+    lib.moe_unpermute_combine_grad.argtypes = [
+        _vp, _vp, _i64, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32,
+        ctypes.POINTER(MoeSpecialExperts), _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     for name in EXPORTS[2:]:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -125,6 +130,13 @@ _F32 = torch.float32
 def moe_permute_workspace_size(T: int, K: int, E: int) -> int:
     n = ctypes.c_size_t(0)
     _check(load().moe_permute_workspace_size(T, K, E, ctypes.byref(n)), "moe_permute_workspace_size")
+    return n.value
+
+
+def moe_unpermute_combine_grad_workspace_size(T: int, H: int, num_const: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().moe_unpermute_combine_grad_workspace_size(T, H, num_const, ctypes.byref(n)),
+           "moe_unpermute_combine_grad_workspace_size")
     return n.value
 
 
@@ -211,6 +223,21 @@ def moe_permute_grad(d_permuted, N, row_of_slot, T, K, H, d_x, stream=None):
         _ptr(d_x, _BF16, "d_x"), _stream(stream)), "moe_permute_grad")
 
 
+def moe_unpermute_combine_grad(grad_out, expert_out, N, row_of_slot, row_map, expert_ids, probs, T,
+                               K, H, num_experts, special, d_expert_out, d_probs, d_ori_x,
+                               d_alpha1, d_alpha2, d_const_v, ws, stream=None):
+    sp = ctypes.byref(special) if special is not None else None
+    _check(load().moe_unpermute_combine_grad(
+        _ptr(grad_out, _BF16, "grad_out"), _ptr(expert_out, _BF16, "expert_out"), N,
+        _ptr(row_of_slot, _I32, "row_of_slot"), _ptr(row_map, _I32, "row_map"),
+        _ptr(expert_ids, _I32, "expert_ids"), _ptr(probs, _F32, "probs"), T, K, H, num_experts, sp,
+        _ptr(d_expert_out, _BF16, "d_expert_out"), _ptr(d_probs, _F32, "d_probs"),
+        _ptr(d_ori_x, _BF16, "d_ori_x"), _ptr(d_alpha1, _F32, "d_alpha1"),
+        _ptr(d_alpha2, _F32, "d_alpha2"), _ptr(d_const_v, _BF16, "d_const_v"),
+        _ptr(ws, None, "workspace"), ws.numel() if ws is not None else 0, _stream(stream)),
+        "moe_unpermute_combine_grad")
+
+
 # --------------------------------------------------------------------------- allocating helpers
 
 def permute_alloc(x, expert_ids, num_experts, *, rows: bool = True, stream=None):
@@ -292,3 +319,34 @@ def permute_grad_alloc(d_permuted, row_of_slot, *, stream=None):
     d_x = torch.empty((T, H), dtype=_BF16, device=d_permuted.device)
     moe_permute_grad(d_permuted, N, row_of_slot, T, K, H, d_x, stream)
     return d_x
+
+
+def combine_grad_alloc(grad_out, expert_out, row_of_slot, expert_ids, probs, num_experts, *,
+                       row_map=None, special=None, alpha_numel=0, d_expert_out=None,
+                       want=("d_expert_out", "d_probs", "d_ori_x", "d_alpha", "d_const_v"),
+                       stream=None):
+    """Backward of the combine. Returns a dict with the requested outputs
+    (d_alpha1 / d_alpha2 as flat fp32 tensors of alpha_numel elements,
+    zero-filled before the call)."""
+    T, K = expert_ids.shape
+    H = grad_out.shape[1]
+    N = expert_out.shape[0] if expert_out is not None else 0
+    dev = grad_out.device
+    nc = special.num_const if special is not None else 0
+    r = {"d_probs": torch.empty((T, K), dtype=_F32, device=dev)}
+    if "d_expert_out" in want:
+        r["d_expert_out"] = (d_expert_out if d_expert_out is not None
+                             else torch.zeros((N, H), dtype=_BF16, device=dev))
+    if "d_ori_x" in want:
+        r["d_ori_x"] = torch.empty((T, H), dtype=_BF16, device=dev)
+    if "d_alpha" in want and nc > 0:
+        r["d_alpha1"] = torch.zeros(alpha_numel, dtype=_F32, device=dev)
+        r["d_alpha2"] = torch.zeros(alpha_numel, dtype=_F32, device=dev)
+    if "d_const_v" in want:
+        r["d_const_v"] = torch.empty((nc, H), dtype=_BF16, device=dev)
+    ws = workspace(moe_unpermute_combine_grad_workspace_size(T, H, nc), dev)
+    moe_unpermute_combine_grad(grad_out, expert_out, N, row_of_slot, row_map, expert_ids, probs, T,
+                               K, H, num_experts, special, r.get("d_expert_out"), r["d_probs"],
+                               r.get("d_ori_x"), r.get("d_alpha1"), r.get("d_alpha2"),
+                               r.get("d_const_v"), ws, stream)
+    return r

@@ -38,6 +38,38 @@ moe_status_t check_h(int32_t H) {
   return MOE_OK;
 }
 
+// The special-expert block of the combine and its backward ([CV2] 参数说明:
+// ori_x is required by copy and const experts, alpha and v by const ones;
+// 约束说明: all expert ids must stay below 2^31 - 1).
+moe_status_t parse_special(const moe_special_experts_t* special, int32_t num_experts, int64_t T,
+                           moe::SpecialArgs* sp) {
+  *sp = moe::SpecialArgs{0, 0, 0, nullptr, nullptr, nullptr, 0, 0, 0, nullptr};
+  if (special == nullptr) return MOE_OK;
+  if (special->num_zero < 0 || special->num_copy < 0 || special->num_const < 0)
+    return MOE_ERR_INVALID_ARG;
+  const int64_t ids_total =
+      int64_t(num_experts) + special->num_zero + special->num_copy + special->num_const;
+  if (ids_total >= INT32_MAX) return MOE_ERR_INVALID_ARG;
+  sp->num_zero = special->num_zero;
+  sp->num_copy = special->num_copy;
+  sp->num_const = special->num_const;
+  if (sp->num_copy + sp->num_const > 0) {
+    if (T > 0 && !row_ok(special->ori_x)) return MOE_ERR_INVALID_ARG;
+    sp->ori_x = u16(special->ori_x);
+  }
+  if (sp->num_const > 0) {
+    if (!word_ok(special->alpha1) || !word_ok(special->alpha2) || !row_ok(special->const_v))
+      return MOE_ERR_INVALID_ARG;
+    sp->alpha1 = special->alpha1;
+    sp->alpha2 = special->alpha2;
+    sp->a_st = special->alpha_stride_t;
+    sp->a_sc = special->alpha_stride_c;
+    sp->a_sh = special->alpha_stride_h;
+    sp->const_v = u16(special->const_v);
+  }
+  return MOE_OK;
+}
+
 }  // namespace
 
 MOE_API const char* moe_status_str(moe_status_t s) {
@@ -177,31 +209,8 @@ MOE_API moe_status_t moe_unpermute_combine(const void* expert_out, int64_t N,
   if (moe_status_t s = check_tk(T, K)) return s;
   if (moe_status_t s = check_h(H)) return s;
   if (num_experts < 1 || N < 0 || N > INT32_MAX) return MOE_ERR_INVALID_ARG;
-  moe::SpecialArgs sp{0, 0, 0, nullptr, nullptr, nullptr, 0, 0, 0, nullptr};
-  if (special != nullptr) {
-    if (special->num_zero < 0 || special->num_copy < 0 || special->num_const < 0)
-      return MOE_ERR_INVALID_ARG;
-    const int64_t ids_total = int64_t(num_experts) + special->num_zero + special->num_copy +
-                              special->num_const;
-    if (ids_total >= INT32_MAX) return MOE_ERR_INVALID_ARG;
-    sp.num_zero = special->num_zero;
-    sp.num_copy = special->num_copy;
-    sp.num_const = special->num_const;
-    if (sp.num_copy + sp.num_const > 0) {
-      if (T > 0 && !row_ok(special->ori_x)) return MOE_ERR_INVALID_ARG;
-      sp.ori_x = u16(special->ori_x);
-    }
-    if (sp.num_const > 0) {
-      if (!word_ok(special->alpha1) || !word_ok(special->alpha2) || !row_ok(special->const_v))
-        return MOE_ERR_INVALID_ARG;
-      sp.alpha1 = special->alpha1;
-      sp.alpha2 = special->alpha2;
-      sp.a_st = special->alpha_stride_t;
-      sp.a_sc = special->alpha_stride_c;
-      sp.a_sh = special->alpha_stride_h;
-      sp.const_v = u16(special->const_v);
-    }
-  }
+  moe::SpecialArgs sp;
+  if (moe_status_t s = parse_special(special, num_experts, T, &sp)) return s;
   if (T > 0) {
     if (!word_ok(row_of_slot) || !word_ok(expert_ids) || !word_ok(probs) || !row_ok(out))
       return MOE_ERR_INVALID_ARG;
@@ -228,6 +237,55 @@ MOE_API moe_status_t moe_permute_grad(const void* d_permuted, int64_t N,
   }
   return hip_status(moe::launch_permute_grad(u16(d_permuted), N, row_of_slot, T, K, H, u16(d_x),
                                              stream));
+}
+
+MOE_API moe_status_t moe_unpermute_combine_grad_workspace_size(int64_t T, int32_t H,
+                                                              int32_t num_const, size_t* bytes) {
+  if (bytes == nullptr || T < 0 || T > INT32_MAX || num_const < 0) return MOE_ERR_INVALID_ARG;
+  if (moe_status_t s = check_h(H)) return s;
+  *bytes = moe::combine_grad_workspace_bytes(T, H, num_const);
+  return MOE_OK;
+}
+
+MOE_API moe_status_t moe_unpermute_combine_grad(
+    const void* grad_out, const void* expert_out, int64_t N, const int32_t* row_of_slot,
+    const int32_t* row_map, const int32_t* expert_ids, const float* probs, int64_t T, int32_t K,
+    int32_t H, int32_t num_experts, const moe_special_experts_t* special, void* d_expert_out,
+    float* d_probs, void* d_ori_x, float* d_alpha1, float* d_alpha2, void* d_const_v,
+    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (moe_status_t s = check_tk(T, K)) return s;
+  if (moe_status_t s = check_h(H)) return s;
+  if (num_experts < 1 || N < 0 || N > INT32_MAX) return MOE_ERR_INVALID_ARG;
+  moe::SpecialArgs sp;
+  if (moe_status_t s = parse_special(special, num_experts, T, &sp)) return s;
+  const bool want_alpha = d_alpha1 != nullptr || d_alpha2 != nullptr;
+  if (T > 0) {
+    if (!row_ok(grad_out) || !word_ok(row_of_slot) || !word_ok(expert_ids) || !word_ok(probs) ||
+        !word_ok(d_probs))
+      return MOE_ERR_INVALID_ARG;
+    if (N > 0 && !row_ok(expert_out)) return MOE_ERR_INVALID_ARG;
+    if (row_map != nullptr && !aligned(row_map, 4)) return MOE_ERR_INVALID_ARG;
+    if (d_expert_out != nullptr && !aligned(d_expert_out, 16)) return MOE_ERR_INVALID_ARG;
+    if (d_ori_x != nullptr && !aligned(d_ori_x, 16)) return MOE_ERR_INVALID_ARG;
+    if (d_const_v != nullptr && !aligned(d_const_v, 16)) return MOE_ERR_INVALID_ARG;
+    if (!aligned(d_alpha1, 4) || !aligned(d_alpha2, 4)) return MOE_ERR_INVALID_ARG;
+  }
+  const moe::AlphaLayout lay = moe::classify_alpha(sp, H);
+  if (want_alpha && lay == moe::AlphaLayout::kOther) return MOE_ERR_UNSUPPORTED;
+  const bool cross_token =
+      sp.num_const > 0 && (d_const_v != nullptr ||
+                           (want_alpha && (lay == moe::AlphaLayout::kSharedAlongH ||
+                                           lay == moe::AlphaLayout::kSharedScalar)));
+  if (T > 0 && cross_token) {
+    if (workspace == nullptr || !aligned(workspace, 16) ||
+        workspace_bytes < moe::combine_grad_workspace_bytes(T, H, sp.num_const))
+      return MOE_ERR_WORKSPACE;
+  }
+  const moe::CombineGradArgs o{u16(d_expert_out), d_probs, u16(d_ori_x), d_alpha1, d_alpha2,
+                               u16(d_const_v)};
+  return hip_status(moe::launch_combine_grad(u16(grad_out), u16(expert_out), N, row_of_slot,
+                                             row_map, expert_ids, probs, T, K, H, num_experts, sp,
+                                             o, workspace, stream));
 }
 
 MOE_API moe_status_t moe_unpermute_grad(const void* grad_out, const void* permuted, int64_t N,

@@ -32,6 +32,30 @@ hipError_t launch_combine(const uint16_t* expert_out, int64_t N, const int32_t* 
                           int64_t T, int K, int H, int E, const SpecialArgs& sp,
                           const uint16_t* shared_x, uint16_t* out, hipStream_t st);
 
+// Outputs of the combine backward (every pointer but d_probs nullable).
+struct CombineGradArgs {
+  uint16_t* d_expert_out;
+  float* d_probs;
+  uint16_t* d_ori_x;
+  float* d_alpha1;
+  float* d_alpha2;
+  uint16_t* d_const_v;
+};
+
+// How the const-expert coefficients are laid out, as far as their gradient
+// is concerned: owned by one token ((t, c) scalars whose spans do not overlap
+// between tokens), shared by all tokens along h ([c, H] rows), shared and
+// constant along h, or anything else (no gradient kernel for it).
+enum class AlphaLayout { kNone, kPerToken, kSharedAlongH, kSharedScalar, kOther };
+AlphaLayout classify_alpha(const SpecialArgs& sp, int H);
+
+size_t combine_grad_workspace_bytes(int64_t T, int H, int num_const);
+hipError_t launch_combine_grad(const uint16_t* grad_out, const uint16_t* expert_out, int64_t N,
+                               const int32_t* row_of_slot, const int32_t* row_map,
+                               const int32_t* ids, const float* probs, int64_t T, int K, int H,
+                               int E, const SpecialArgs& sp, const CombineGradArgs& o, void* ws,
+                               hipStream_t st);
+
 hipError_t launch_permute_grad(const uint16_t* d_permuted, int64_t N, const int32_t* row_of_slot,
                                int64_t T, int K, int H, uint16_t* d_x, hipStream_t st);
 

@@ -104,10 +104,26 @@ def f64_to_bf16_scalar(value: float) -> int:
 
 # --------------------------------------------------------------------------- permute
 
-def permute(x, expert_ids, E: int, *, rows: bool = True):
-    """Stable expert-major permute. Returns dict(permuted, sorted_slot,
-    row_of_slot, expert_counts, expert_offsets)."""
+def _mask_slots(expert_ids, active_mask):
+    """x_active_mask ("torch_npu.npu_moe_distribute_combine_v2", 参数说明): a
+    [T] mask marks whole tokens, a [T, K] mask single slots, as taking part in
+    the exchange. A slot that does not take part is never sent to its expert
+    and never comes back: it is a dropped slot, id -1 (no row, no term)."""
     ids = _c(expert_ids, np.int32)
+    if active_mask is None:
+        return ids
+    m = np.asarray(active_mask).astype(bool)
+    if m.ndim == 1:
+        m = np.repeat(m[:, None], ids.shape[1], axis=1)
+    assert m.shape == ids.shape, (m.shape, ids.shape)
+    return np.where(m, ids, np.int32(-1)).astype(np.int32)
+
+
+def permute(x, expert_ids, E: int, *, rows: bool = True, active_mask=None):
+    """Stable expert-major permute. Returns dict(permuted, sorted_slot,
+    row_of_slot, expert_counts, expert_offsets). Slots outside active_mask
+    (optional, [T] or [T, K]) are not routed."""
+    ids = _mask_slots(expert_ids, active_mask)
     T, K = ids.shape
     xx = _c(x, np.uint16) if rows else None
     H = xx.shape[1] if rows else 1
@@ -197,9 +213,11 @@ def grouped_swiglu(x, expert_offsets, w_gate, w_up, w_down, *, want_h: bool = Tr
 def combine(expert_out, row_of_slot, expert_ids, probs, E: int, *, row_map=None,
             num_zero: int = 0, num_copy: int = 0, num_const: int = 0, ori_x=None,
             alpha1=None, alpha2=None, alpha_strides=(0, 0, 0), const_v=None, shared_x=None,
-            H: int | None = None):
-    """Weighted unpermute-combine. Returns (out bf16 bits [T,H], out_f64 [T,H])."""
-    ids = _c(expert_ids, np.int32)
+            H: int | None = None, active_mask=None):
+    """Weighted unpermute-combine. Returns (out bf16 bits [T,H], out_f64 [T,H]).
+    Slots outside active_mask (optional, [T] or [T, K]) add no term; the
+    shared row is still added."""
+    ids = _mask_slots(expert_ids, active_mask)
     T, K = ids.shape
     ros = _c(row_of_slot, np.int32)
     pr = _c(probs, np.float32)
@@ -269,13 +287,14 @@ def permute_grad(d_permuted, row_of_slot):
 
 def combine_grad(grad_out, expert_out, row_of_slot, expert_ids, probs, E: int, *, row_map=None,
                  num_zero: int = 0, num_copy: int = 0, num_const: int = 0, ori_x=None,
-                 alpha1=None, alpha2=None, alpha_strides=(0, 0, 0), const_v=None):
+                 alpha1=None, alpha2=None, alpha_strides=(0, 0, 0), const_v=None,
+                 active_mask=None):
     """Backward of combine() (special and shared experts included), all in fp64.
     Returns a dict: d_expert_out [N,H] (0 in rows no slot references), row_written
     [N] bool, d_probs [T,K], d_ori_x [T,H], d_alpha1 / d_alpha2 (alpha's flat
     layout), d_const_v [num_const,H], d_shared [T,H]."""
     g = _c(grad_out, np.uint16)
-    ids = _c(expert_ids, np.int32)
+    ids = _mask_slots(expert_ids, active_mask)
     T, K = ids.shape
     H = g.shape[1]
     ros = _c(row_of_slot, np.int32)

@@ -272,7 +272,24 @@ def run_ops(args, dev, flush):
     ops.append(dict(workload=c["name"], **op_entry("unpermute_combine",
                                                    *time_op(f_comb, args.op_iters, flush),
                                                    nbytes=combine_bytes(T, K, H, N))))
-    del x, p, out
+    # the same with x_active_mask: a [T, K] slot mask with 10% of the slots off
+    m_np = np.random.default_rng(22).random((T, K)) < 0.9
+    mask = torch.from_numpy(m_np).to(dev)
+    pm = moe.permute_alloc(x, ids, E, active_mask=mask)
+    Nm = int(pm["expert_offsets"][-1].item())
+    f_permm = lambda: moe.moe_permute(x, ids, T, H, K, E, pm["permuted"], pm["sorted_slot"],
+                                      pm["row_of_slot"], pm["expert_counts"],
+                                      pm["expert_offsets"], ws, active_mask=mask)
+    f_combm = lambda: moe.moe_unpermute_combine(pm["permuted"], T * K, pm["row_of_slot"], None, ids,
+                                                probs, T, K, H, E, None, None, out,
+                                                active_mask=mask)
+    ops.append(dict(workload=c["name"] + "_slotmask90", **op_entry(
+        "permute_masked", *time_op(f_permm, args.op_iters, flush),
+        nbytes=permute_bytes(T, K, H, Nm) + T * K)))
+    ops.append(dict(workload=c["name"] + "_slotmask90", **op_entry(
+        "unpermute_combine_masked", *time_op(f_combm, args.op_iters, flush),
+        nbytes=combine_bytes(T, K, H, Nm) + T * K)))
+    del x, p, pm, out
     # reorder + combine with special experts, R=8 x E_local=32, N=32768, H=4096
     g = W.gen_c4()
     c = g["cfg"]

@@ -79,10 +79,15 @@ int32_t moe_abi_version(void);
  * bucketed by id, stably: the row of slot s is
  *     expert_offsets[id] + #{ s' < s : id(s') == id }.
  * Slots whose id is outside [0, E) (special experts of [CV2], which own no
- * row) get row_of_slot = -1.
+ * row) get row_of_slot = -1, and so do slots outside the active mask.
  *
  *  x              bf16 [T, H]                       in  (may be NULL iff permuted is NULL)
  *  expert_ids     int32 [T, K]                      in
+ *  active_mask    uint8 [T] or [T, K]               in  (nullable: every slot takes part)
+ *  mask_per_slot  0: active_mask is [T], one flag per token; 1: [T, K], one per slot
+ *                 ([CV2] 参数说明 x_active_mask: nonzero = the token / slot takes
+ *                 part in the exchange; a [T] mask should hold its trues first,
+ *                 but any pattern is applied flag by flag)
  *  permuted       bf16 [T*K, H] capacity            out rows [0, N) written, N = expert_offsets[E];
  *                                                       NULL: index maps only
  *  sorted_slot    int32 [T*K]                       out row -> slot, -1 for rows [N, T*K)
@@ -91,12 +96,13 @@ int32_t moe_abi_version(void);
  *  expert_offsets int32 [E+1]                       out exclusive prefix, [E] = N
  *  workspace      >= moe_permute_workspace_size(T, K, E)
  * Errors: INVALID_ARG for T < 0, K outside [1,16], E outside [1,1024], H <= 0,
- * T*K > INT32_MAX, a required pointer NULL or misaligned; UNSUPPORTED for
- * H % 8 != 0; WORKSPACE if too small.
+ * T*K > INT32_MAX, mask_per_slot not 0 or 1, a required pointer NULL or
+ * misaligned; UNSUPPORTED for H % 8 != 0; WORKSPACE if too small.
  * ------------------------------------------------------------------------ */
 moe_status_t moe_permute_workspace_size(int64_t T, int32_t K, int32_t E, size_t* bytes);
-moe_status_t moe_permute(const void* x, const int32_t* expert_ids, int64_t T, int32_t H,
-                         int32_t K, int32_t num_experts, void* permuted, int32_t* sorted_slot,
+moe_status_t moe_permute(const void* x, const int32_t* expert_ids, const uint8_t* active_mask,
+                         int32_t mask_per_slot, int64_t T, int32_t H, int32_t K,
+                         int32_t num_experts, void* permuted, int32_t* sorted_slot,
                          int32_t* row_of_slot, int32_t* expert_counts, int32_t* expert_offsets,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
@@ -185,6 +191,9 @@ moe_status_t moe_grouped_gemm_swiglu(const void* x, const int32_t* expert_offset
  *  expert_out   bf16 [N, H]   in (may be NULL iff N == 0)
  *  row_of_slot  int32 [T*K]   in     row_map  int32 [N] in (nullable)
  *  expert_ids   int32 [T*K]   in     probs    fp32 [T*K] in (any sign, any sum)
+ *  active_mask  uint8 [T] or [T*K] in (nullable), mask_per_slot as for
+ *               moe_permute: a slot outside the mask adds no term (the shared
+ *               row is still added)
  *  special      nullable: no special experts. Its ori_x is bf16 [T,H]
  *               (required if num_copy + num_const > 0); alpha1 / alpha2 are
  *               fp32 with element (t, c, h) at t*alpha_stride_t +
@@ -197,7 +206,8 @@ moe_status_t moe_grouped_gemm_swiglu(const void* x, const int32_t* expert_offset
  * Errors: INVALID_ARG for T < 0, K outside [1,16], H <= 0, E < 1, N < 0,
  * negative special counts, E+Z+C+Nc >= 2^31-1 ([CV2] 约束说明), T*K >
  * INT32_MAX, N > INT32_MAX, missing ori_x / alpha / const_v ([CV2] 参数说明),
- * NULL / misaligned pointers; UNSUPPORTED for H % 8 != 0.
+ * mask_per_slot not 0 or 1, NULL / misaligned pointers; UNSUPPORTED for
+ * H % 8 != 0.
  * ------------------------------------------------------------------------ */
 typedef struct moe_special_experts {
     int32_t num_zero;
@@ -214,7 +224,8 @@ typedef struct moe_special_experts {
 
 moe_status_t moe_unpermute_combine(const void* expert_out, int64_t N, const int32_t* row_of_slot,
                                    const int32_t* row_map, const int32_t* expert_ids,
-                                   const float* probs, int64_t T, int32_t K, int32_t H,
+                                   const float* probs, const uint8_t* active_mask,
+                                   int32_t mask_per_slot, int64_t T, int32_t K, int32_t H,
                                    int32_t num_experts, const moe_special_experts_t* special,
                                    const void* shared_x, void* out, hipStream_t stream);
 
@@ -245,7 +256,9 @@ moe_status_t moe_unpermute_combine(const void* expert_out, int64_t N, const int3
  * per-segment partials in the workspace, added in a fixed order: the result
  * is deterministic.
  *
- *  grad_out      bf16 [T, H]   in          (the other inputs as for the combine)
+ *  grad_out      bf16 [T, H]   in          (the other inputs, active_mask
+ *                                          included, as for the combine; slots
+ *                                          outside the mask get d_probs = 0)
  *  d_expert_out  bf16 [N, H]   out (nullable: not computed)
  *  d_probs       fp32 [T*K]    out
  *  d_ori_x       bf16 [T, H]   out (nullable); zero rows for tokens without
@@ -263,8 +276,9 @@ moe_status_t moe_unpermute_combine_grad_workspace_size(int64_t T, int32_t H, int
                                                       size_t* bytes);
 moe_status_t moe_unpermute_combine_grad(
     const void* grad_out, const void* expert_out, int64_t N, const int32_t* row_of_slot,
-    const int32_t* row_map, const int32_t* expert_ids, const float* probs, int64_t T, int32_t K,
-    int32_t H, int32_t num_experts, const moe_special_experts_t* special, void* d_expert_out,
+    const int32_t* row_map, const int32_t* expert_ids, const float* probs,
+    const uint8_t* active_mask, int32_t mask_per_slot, int64_t T, int32_t K, int32_t H,
+    int32_t num_experts, const moe_special_experts_t* special, void* d_expert_out,
     float* d_probs, void* d_ori_x, float* d_alpha1, float* d_alpha2, void* d_const_v,
     void* workspace, size_t workspace_bytes, hipStream_t stream);
 

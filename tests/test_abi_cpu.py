@@ -84,8 +84,9 @@ PM = P + 2         # misaligned
 
 
 def _permute(lib, x=P, ids=P, T=16, H=64, K=2, E=4, perm=P, ss=P, ros=P, cnt=P, off=P, ws=P,
-             wsb=1 << 20):
-    return lib.moe_permute(x, ids, T, H, K, E, perm, ss, ros, cnt, off, ws, wsb, None)
+             wsb=1 << 20, mask=None, per_slot=0):
+    return lib.moe_permute(x, ids, mask, per_slot, T, H, K, E, perm, ss, ros, cnt, off, ws, wsb,
+                           None)
 
 
 @no_gpu
@@ -105,6 +106,7 @@ def test_permute_checks(lib):
     assert _permute(lib, cnt=None) == INVALID
     assert _permute(lib, ws=None) == WORKSPACE
     assert _permute(lib, wsb=4) == WORKSPACE
+    assert _permute(lib, mask=P, per_slot=2) == INVALID
 
 
 def _reorder(lib, x=P, cnt=P, R=8, El=32, N=1000, H=64, y=P, perm=P, inv=P, tpe=P, off=P, ws=P,
@@ -150,12 +152,12 @@ def test_gemm_checks(lib):
 
 
 def _combine(lib, eo=P, N=100, ros=P, rmap=None, ids=P, probs=P, T=50, K=2, H=64, E=8, sp=None,
-             shared=None, out=P):
+             shared=None, out=P, mask=None, per_slot=0):
     from unpermute_combine_moe_amd.binding import MoeSpecialExperts
 
     spp = ctypes.byref(sp) if isinstance(sp, MoeSpecialExperts) else None
-    return lib.moe_unpermute_combine(eo, N, ros, rmap, ids, probs, T, K, H, E, spp, shared, out,
-                                     None)
+    return lib.moe_unpermute_combine(eo, N, ros, rmap, ids, probs, mask, per_slot, T, K, H, E, spp,
+                                     shared, out, None)
 
 
 @no_gpu
@@ -170,6 +172,7 @@ def test_combine_checks(lib):
     assert _combine(lib, eo=None) == INVALID
     assert _combine(lib, out=P + 2) == INVALID
     assert _combine(lib, rmap=PM) == INVALID
+    assert _combine(lib, mask=P, per_slot=-1) == INVALID
     assert _combine(lib, shared=P + 8) == INVALID
     # the combine_v2 page: ori_x is required by copy / const experts, alpha and v by const ones
     assert _combine(lib, sp=S(0, 1, 0, None, None, None, 0, 0, 0, None)) == INVALID
@@ -213,10 +216,11 @@ def test_permute_grad_checks(lib):
 
 
 def _cgrad(lib, g=P, eo=P, N=100, ros=P, rmap=None, ids=P, probs=P, T=50, K=2, H=64, E=8,
-           sp=None, deo=P, dpr=P, dori=P, da1=None, da2=None, dcv=None, ws=P, wsb=1 << 24):
+           sp=None, deo=P, dpr=P, dori=P, da1=None, da2=None, dcv=None, ws=P, wsb=1 << 24,
+           mask=None, per_slot=0):
     spp = ctypes.byref(sp) if sp is not None else None
-    return lib.moe_unpermute_combine_grad(g, eo, N, ros, rmap, ids, probs, T, K, H, E, spp, deo,
-                                          dpr, dori, da1, da2, dcv, ws, wsb, None)
+    return lib.moe_unpermute_combine_grad(g, eo, N, ros, rmap, ids, probs, mask, per_slot, T, K,
+                                          H, E, spp, deo, dpr, dori, da1, da2, dcv, ws, wsb, None)
 
 
 @no_gpu
@@ -229,6 +233,7 @@ def test_combine_grad_checks(lib):
     assert _cgrad(lib, T=-1) == INVALID
     assert _cgrad(lib, K=17) == INVALID
     assert _cgrad(lib, H=12) == UNSUPPORTED
+    assert _cgrad(lib, mask=P, per_slot=3) == INVALID
     assert _cgrad(lib, g=None) == INVALID
     assert _cgrad(lib, dpr=None) == INVALID
     assert _cgrad(lib, deo=P + 2) == INVALID

@@ -68,21 +68,22 @@ def load(path: str = LIB_PATH):
     lib.moe_abi_version.restype = _i32
     sz = ctypes.POINTER(ctypes.c_size_t)
     lib.moe_permute_workspace_size.argtypes = [_i64, _i32, _i32, sz]
-    lib.moe_permute.argtypes = [_vp, _vp, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
-                                ctypes.c_size_t, _vp]
+    lib.moe_permute.argtypes = [_vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
+                                _vp, _vp, ctypes.c_size_t, _vp]
     lib.moe_rank_to_expert_reorder_workspace_size.argtypes = [_i32, _i32, sz]
     lib.moe_rank_to_expert_reorder.argtypes = [_vp, _vp, _i32, _i32, _i64, _i32, _vp, _vp, _vp,
                                                _vp, _vp, _vp, ctypes.c_size_t, _vp]
     lib.moe_grouped_gemm_swiglu_workspace_size.argtypes = [_i32, _i64, _i32, _i32, sz]
     lib.moe_grouped_gemm_swiglu.argtypes = [_vp, _vp, _i32, _i64, _i32, _i32, _vp, _vp, _vp, _vp,
                                             _vp, _vp, ctypes.c_size_t, _vp]
-    lib.moe_unpermute_combine.argtypes = [_vp, _i64, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32,
-                                          ctypes.POINTER(MoeSpecialExperts), _vp, _vp, _vp]
+    lib.moe_unpermute_combine.argtypes = [_vp, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32,
+                                          _i32, _i32, ctypes.POINTER(MoeSpecialExperts), _vp, _vp,
+                                          _vp]
     lib.moe_unpermute_grad.argtypes = [_vp, _vp, _i64, _vp, _vp, _i64, _i32, _i32, _vp, _vp, _vp]
     lib.moe_permute_grad.argtypes = [_vp, _i64, _vp, _i64, _i32, _i32, _vp, _vp]
     lib.moe_unpermute_combine_grad_workspace_size.argtypes = [_i64, _i32, _i32, sz]
     lib.moe_unpermute_combine_grad.argtypes = [
-        _vp, _vp, _i64, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32,
+        _vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32,
         ctypes.POINTER(MoeSpecialExperts), _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
     for name in EXPORTS[2:]:
         getattr(lib, name).restype = ctypes.c_int
@@ -160,10 +161,28 @@ def workspace(nbytes: int, device) -> torch.Tensor:
 
 # --------------------------------------------------------------------------- calls
 
+def _mask(active_mask, T, K):
+    """(pointer, per_slot) of an optional x_active_mask: bool or uint8, [T] or [T, K]."""
+    if active_mask is None:
+        return None, 0
+    if active_mask.dtype not in (torch.bool, torch.uint8):
+        raise TypeError(f"active_mask: expected bool or uint8, got {active_mask.dtype}")
+    if tuple(active_mask.shape) == (T,):
+        per_slot = 0
+    elif tuple(active_mask.shape) == (T, K):
+        per_slot = 1
+    else:
+        raise ValueError(f"active_mask: expected shape ({T},) or ({T}, {K}), "
+                         f"got {tuple(active_mask.shape)}")
+    return _ptr(active_mask, None, "active_mask"), per_slot
+
+
 def moe_permute(x, expert_ids, T, H, K, num_experts, permuted, sorted_slot, row_of_slot,
-                expert_counts, expert_offsets, ws, stream=None):
+                expert_counts, expert_offsets, ws, stream=None, *, active_mask=None):
+    mp, per_slot = _mask(active_mask, T, K)
     _check(load().moe_permute(
-        _ptr(x, _BF16, "x"), _ptr(expert_ids, _I32, "expert_ids"), T, H, K, num_experts,
+        _ptr(x, _BF16, "x"), _ptr(expert_ids, _I32, "expert_ids"), mp, per_slot, T, H, K,
+        num_experts,
         _ptr(permuted, _BF16, "permuted"), _ptr(sorted_slot, _I32, "sorted_slot"),
         _ptr(row_of_slot, _I32, "row_of_slot"), _ptr(expert_counts, _I32, "expert_counts"),
         _ptr(expert_offsets, _I32, "expert_offsets"), _ptr(ws, None, "workspace"),
@@ -199,12 +218,13 @@ def make_special(num_zero=0, num_copy=0, num_const=0, ori_x=None, alpha1=None, a
 
 
 def moe_unpermute_combine(expert_out, N, row_of_slot, row_map, expert_ids, probs, T, K, H,
-                          num_experts, special, shared_x, out, stream=None):
+                          num_experts, special, shared_x, out, stream=None, *, active_mask=None):
     sp = ctypes.byref(special) if special is not None else None
+    mp, per_slot = _mask(active_mask, T, K)
     _check(load().moe_unpermute_combine(
         _ptr(expert_out, _BF16, "expert_out"), N, _ptr(row_of_slot, _I32, "row_of_slot"),
         _ptr(row_map, _I32, "row_map"), _ptr(expert_ids, _I32, "expert_ids"),
-        _ptr(probs, _F32, "probs"), T, K, H, num_experts, sp, _ptr(shared_x, _BF16, "shared_x"),
+        _ptr(probs, _F32, "probs"), mp, per_slot, T, K, H, num_experts, sp, _ptr(shared_x, _BF16, "shared_x"),
         _ptr(out, _BF16, "out"), _stream(stream)), "moe_unpermute_combine")
 
 
@@ -225,12 +245,14 @@ def moe_permute_grad(d_permuted, N, row_of_slot, T, K, H, d_x, stream=None):
 
 def moe_unpermute_combine_grad(grad_out, expert_out, N, row_of_slot, row_map, expert_ids, probs, T,
                                K, H, num_experts, special, d_expert_out, d_probs, d_ori_x,
-                               d_alpha1, d_alpha2, d_const_v, ws, stream=None):
+                               d_alpha1, d_alpha2, d_const_v, ws, stream=None, *, active_mask=None):
     sp = ctypes.byref(special) if special is not None else None
+    mp, per_slot = _mask(active_mask, T, K)
     _check(load().moe_unpermute_combine_grad(
         _ptr(grad_out, _BF16, "grad_out"), _ptr(expert_out, _BF16, "expert_out"), N,
         _ptr(row_of_slot, _I32, "row_of_slot"), _ptr(row_map, _I32, "row_map"),
-        _ptr(expert_ids, _I32, "expert_ids"), _ptr(probs, _F32, "probs"), T, K, H, num_experts, sp,
+        _ptr(expert_ids, _I32, "expert_ids"), _ptr(probs, _F32, "probs"), mp, per_slot, T, K, H,
+        num_experts, sp,
         _ptr(d_expert_out, _BF16, "d_expert_out"), _ptr(d_probs, _F32, "d_probs"),
         _ptr(d_ori_x, _BF16, "d_ori_x"), _ptr(d_alpha1, _F32, "d_alpha1"),
         _ptr(d_alpha2, _F32, "d_alpha2"), _ptr(d_const_v, _BF16, "d_const_v"),
@@ -240,7 +262,7 @@ def moe_unpermute_combine_grad(grad_out, expert_out, N, row_of_slot, row_map, ex
 
 # --------------------------------------------------------------------------- allocating helpers
 
-def permute_alloc(x, expert_ids, num_experts, *, rows: bool = True, stream=None):
+def permute_alloc(x, expert_ids, num_experts, *, rows: bool = True, active_mask=None, stream=None):
     T, K = expert_ids.shape
     dev = expert_ids.device
     H = x.shape[1] if rows else 0
@@ -255,7 +277,7 @@ def permute_alloc(x, expert_ids, num_experts, *, rows: bool = True, stream=None)
     ws = workspace(moe_permute_workspace_size(T, K, num_experts), dev)
     moe_permute(x if rows else None, expert_ids, T, H, K, num_experts, out["permuted"],
                 out["sorted_slot"], out["row_of_slot"], out["expert_counts"],
-                out["expert_offsets"], ws, stream)
+                out["expert_offsets"], ws, stream, active_mask=active_mask)
     return out
 
 
@@ -291,14 +313,14 @@ def grouped_gemm_alloc(x, expert_offsets, w_gate, w_up, w_down, *, stream=None):
 
 
 def combine_alloc(expert_out, row_of_slot, expert_ids, probs, num_experts, *, row_map=None,
-                  special=None, shared_x=None, H=None, stream=None):
+                  special=None, shared_x=None, H=None, active_mask=None, stream=None):
     T, K = expert_ids.shape
     if H is None:
         H = expert_out.shape[1]
     N = expert_out.shape[0] if expert_out is not None else 0
     out = torch.empty((T, H), dtype=_BF16, device=expert_ids.device)
     moe_unpermute_combine(expert_out, N, row_of_slot, row_map, expert_ids, probs, T, K, H,
-                          num_experts, special, shared_x, out, stream)
+                          num_experts, special, shared_x, out, stream, active_mask=active_mask)
     return out
 
 
@@ -324,7 +346,7 @@ def permute_grad_alloc(d_permuted, row_of_slot, *, stream=None):
 def combine_grad_alloc(grad_out, expert_out, row_of_slot, expert_ids, probs, num_experts, *,
                        row_map=None, special=None, alpha_numel=0, d_expert_out=None,
                        want=("d_expert_out", "d_probs", "d_ori_x", "d_alpha", "d_const_v"),
-                       stream=None):
+                       active_mask=None, stream=None):
     """Backward of the combine. Returns a dict with the requested outputs
     (d_alpha1 / d_alpha2 as flat fp32 tensors of alpha_numel elements,
     zero-filled before the call)."""
@@ -348,5 +370,5 @@ def combine_grad_alloc(grad_out, expert_out, row_of_slot, expert_ids, probs, num
     moe_unpermute_combine_grad(grad_out, expert_out, N, row_of_slot, row_map, expert_ids, probs, T,
                                K, H, num_experts, special, r.get("d_expert_out"), r["d_probs"],
                                r.get("d_ori_x"), r.get("d_alpha1"), r.get("d_alpha2"),
-                               r.get("d_const_v"), ws, stream)
+                               r.get("d_const_v"), ws, stream, active_mask=active_mask)
     return r

@@ -95,8 +95,9 @@ MOE_API moe_status_t moe_permute_workspace_size(int64_t T, int32_t K, int32_t E,
   return MOE_OK;
 }
 
-MOE_API moe_status_t moe_permute(const void* x, const int32_t* expert_ids, int64_t T, int32_t H,
-                                 int32_t K, int32_t num_experts, void* permuted,
+MOE_API moe_status_t moe_permute(const void* x, const int32_t* expert_ids,
+                                 const uint8_t* active_mask, int32_t mask_per_slot, int64_t T,
+                                 int32_t H, int32_t K, int32_t num_experts, void* permuted,
                                  int32_t* sorted_slot, int32_t* row_of_slot,
                                  int32_t* expert_counts, int32_t* expert_offsets, void* workspace,
                                  size_t workspace_bytes, hipStream_t stream) {
@@ -111,10 +112,12 @@ MOE_API moe_status_t moe_permute(const void* x, const int32_t* expert_ids, int64
       return MOE_ERR_INVALID_ARG;
     if (permuted != nullptr && (!row_ok(x) || !row_ok(permuted))) return MOE_ERR_INVALID_ARG;
   }
+  if (mask_per_slot != 0 && mask_per_slot != 1) return MOE_ERR_INVALID_ARG;
   const size_t need = moe::permute_workspace_bytes(T, K, num_experts);
   if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 4))
     return MOE_ERR_WORKSPACE;
-  return hip_status(moe::launch_permute(u16(x), expert_ids, T, H, K, num_experts, u16(permuted),
+  const moe::SlotMask mk{active_mask, mask_per_slot, K};
+  return hip_status(moe::launch_permute(u16(x), expert_ids, mk, T, H, K, num_experts, u16(permuted),
                                         sorted_slot, row_of_slot, expert_counts, expert_offsets,
                                         workspace, stream));
 }
@@ -203,6 +206,7 @@ MOE_API moe_status_t moe_grouped_gemm_swiglu(const void* x, const int32_t* exper
 MOE_API moe_status_t moe_unpermute_combine(const void* expert_out, int64_t N,
                                            const int32_t* row_of_slot, const int32_t* row_map,
                                            const int32_t* expert_ids, const float* probs,
+                                           const uint8_t* active_mask, int32_t mask_per_slot,
                                            int64_t T, int32_t K, int32_t H, int32_t num_experts,
                                            const moe_special_experts_t* special,
                                            const void* shared_x, void* out, hipStream_t stream) {
@@ -218,8 +222,10 @@ MOE_API moe_status_t moe_unpermute_combine(const void* expert_out, int64_t N,
     if (row_map != nullptr && !aligned(row_map, 4)) return MOE_ERR_INVALID_ARG;
     if (shared_x != nullptr && !aligned(shared_x, 16)) return MOE_ERR_INVALID_ARG;
   }
+  if (mask_per_slot != 0 && mask_per_slot != 1) return MOE_ERR_INVALID_ARG;
+  const moe::SlotMask mk{active_mask, mask_per_slot, K};
   return hip_status(moe::launch_combine(u16(expert_out), N, row_of_slot, row_map, expert_ids,
-                                        probs, T, K, H, num_experts, sp, u16(shared_x), u16(out),
+                                        probs, mk, T, K, H, num_experts, sp, u16(shared_x), u16(out),
                                         stream));
 }
 
@@ -249,8 +255,9 @@ MOE_API moe_status_t moe_unpermute_combine_grad_workspace_size(int64_t T, int32_
 
 MOE_API moe_status_t moe_unpermute_combine_grad(
     const void* grad_out, const void* expert_out, int64_t N, const int32_t* row_of_slot,
-    const int32_t* row_map, const int32_t* expert_ids, const float* probs, int64_t T, int32_t K,
-    int32_t H, int32_t num_experts, const moe_special_experts_t* special, void* d_expert_out,
+    const int32_t* row_map, const int32_t* expert_ids, const float* probs,
+    const uint8_t* active_mask, int32_t mask_per_slot, int64_t T, int32_t K, int32_t H,
+    int32_t num_experts, const moe_special_experts_t* special, void* d_expert_out,
     float* d_probs, void* d_ori_x, float* d_alpha1, float* d_alpha2, void* d_const_v,
     void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (moe_status_t s = check_tk(T, K)) return s;
@@ -270,6 +277,7 @@ MOE_API moe_status_t moe_unpermute_combine_grad(
     if (d_const_v != nullptr && !aligned(d_const_v, 16)) return MOE_ERR_INVALID_ARG;
     if (!aligned(d_alpha1, 4) || !aligned(d_alpha2, 4)) return MOE_ERR_INVALID_ARG;
   }
+  if (mask_per_slot != 0 && mask_per_slot != 1) return MOE_ERR_INVALID_ARG;
   const moe::AlphaLayout lay = moe::classify_alpha(sp, H);
   if (want_alpha && lay == moe::AlphaLayout::kOther) return MOE_ERR_UNSUPPORTED;
   const bool cross_token =
@@ -281,10 +289,12 @@ MOE_API moe_status_t moe_unpermute_combine_grad(
         workspace_bytes < moe::combine_grad_workspace_bytes(T, H, sp.num_const))
       return MOE_ERR_WORKSPACE;
   }
+  const moe::SlotMask mk{active_mask, mask_per_slot, K};
   const moe::CombineGradArgs o{u16(d_expert_out), d_probs, u16(d_ori_x), d_alpha1, d_alpha2,
                                u16(d_const_v)};
   return hip_status(moe::launch_combine_grad(u16(grad_out), u16(expert_out), N, row_of_slot,
-                                             row_map, expert_ids, probs, T, K, H, num_experts, sp,
+                                             row_map, expert_ids, probs, mk, T, K, H, num_experts,
+                                             sp,
                                              o, workspace, stream));
 }
 

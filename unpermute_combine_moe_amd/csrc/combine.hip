@@ -31,8 +31,8 @@ template <bool kHasRowMap, bool kAlphaPerH, bool kUnit = false>
 __global__ void __launch_bounds__(kWaves * kWave)
 k_combine(const uint16_t* __restrict__ expert_out, int64_t N, const int32_t* __restrict__ row_of_slot,
           const int32_t* __restrict__ row_map, const int32_t* __restrict__ ids,
-          const float* __restrict__ probs, int64_t T, int K, int H, int E, SpecialArgs sp,
-          const uint16_t* __restrict__ shared_x, uint16_t* __restrict__ out) {
+          const float* __restrict__ probs, SlotMask mk, int64_t T, int K, int H, int E,
+          SpecialArgs sp, const uint16_t* __restrict__ shared_x, uint16_t* __restrict__ out) {
   const int64_t t = uniform(static_cast<int>(blockIdx.x * kWaves + threadIdx.x / kWave));
   if (t >= T) return;
   const int lane = threadIdx.x % kWave;
@@ -53,7 +53,8 @@ k_combine(const uint16_t* __restrict__ expert_out, int64_t N, const int32_t* __r
     }
   } else if (lane < K) {
     const int64_t s = t * K + lane;
-    const int id = ids[s];
+    const int id_in = ids[s];
+    const int id = mk.active(s) ? id_in : -1;  // a slot outside the mask is dropped
     m_p = probs[s];
     if (id >= 0 && id < E) {
       int64_t row = row_of_slot[s];
@@ -145,7 +146,7 @@ k_combine(const uint16_t* __restrict__ expert_out, int64_t N, const int32_t* __r
 
 hipError_t launch_combine(const uint16_t* expert_out, int64_t N, const int32_t* row_of_slot,
                           const int32_t* row_map, const int32_t* ids, const float* probs,
-                          int64_t T, int K, int H, int E, const SpecialArgs& sp,
+                          SlotMask mk, int64_t T, int K, int H, int E, const SpecialArgs& sp,
                           const uint16_t* shared_x, uint16_t* out, hipStream_t st) {
   if (T == 0) return hipGetLastError();
   const dim3 grid(static_cast<unsigned>(ceil_div(T, kWaves)));
@@ -153,7 +154,7 @@ hipError_t launch_combine(const uint16_t* expert_out, int64_t N, const int32_t* 
   const bool per_h = sp.num_const > 0 && sp.a_sh != 0;
 #define MOE_COMBINE(RM, PH)                                                                    \
   hipLaunchKernelGGL((k_combine<RM, PH>), grid, block, 0, st, expert_out, N, row_of_slot,     \
-                     row_map, ids, probs, T, K, H, E, sp, shared_x, out)
+                     row_map, ids, probs, mk, T, K, H, E, sp, shared_x, out)
   if (row_map != nullptr) {
     if (per_h) MOE_COMBINE(true, true); else MOE_COMBINE(true, false);
   } else {
@@ -169,8 +170,8 @@ hipError_t launch_permute_grad(const uint16_t* d_permuted, int64_t N, const int3
   const dim3 grid(static_cast<unsigned>(ceil_div(T, kWaves)));
   const dim3 block(kWaves * kWave);
   hipLaunchKernelGGL((k_combine<false, false, true>), grid, block, 0, st, d_permuted, N,
-                     row_of_slot, nullptr, nullptr, nullptr, T, K, H, 0, SpecialArgs{}, nullptr,
-                     d_x);
+                     row_of_slot, nullptr, nullptr, nullptr, SlotMask{nullptr, 0, K}, T, K, H, 0,
+                     SpecialArgs{}, nullptr, d_x);
   return hipGetLastError();
 }
 

@@ -38,8 +38,8 @@ __global__ void __launch_bounds__(kWaves * kWave)
 k_combine_grad(const uint16_t* __restrict__ grad_out, const uint16_t* __restrict__ expert_out,
                int64_t N, const int32_t* __restrict__ row_of_slot,
                const int32_t* __restrict__ row_map, const int32_t* __restrict__ ids,
-               const float* __restrict__ probs, int64_t T, int K, int H, int E, SpecialArgs sp,
-               CombineGradArgs o, int alpha_token, int nsplit) {
+               const float* __restrict__ probs, SlotMask mk, int64_t T, int K, int H, int E,
+               SpecialArgs sp, CombineGradArgs o, int alpha_token, int nsplit) {
   // nsplit waves share a token, each taking every nsplit-th 64-chunk row of
   // the hidden dim; their per-slot sums meet in LDS
   __shared__ float xch[kWaves][2][kMaxK];
@@ -58,7 +58,8 @@ k_combine_grad(const uint16_t* __restrict__ grad_out, const uint16_t* __restrict
   float m_p = 0.f, m_a1 = 0.f, m_a2 = 0.f;
   if (live && lane < K) {
     const int64_t s = t * K + lane;
-    const int id = ids[s];
+    const int id_in = ids[s];
+    const int id = mk.active(s) ? id_in : -1;  // a slot outside the mask is dropped
     m_p = probs[s];
     if (id >= 0 && id < E) {
       int64_t row = row_of_slot[s];
@@ -240,7 +241,7 @@ constexpr int batch_slots() { return kSharedAlpha ? 4 : 8; }
 template <bool kAlphaPerH, bool kSharedAlpha>
 __global__ void __launch_bounds__(kWaves * kWave)
 k_const_grad_partial(const uint16_t* __restrict__ grad_out, const int32_t* __restrict__ ids,
-                     const float* __restrict__ probs, int64_t T, int K, int H, int E,
+                     const float* __restrict__ probs, SlotMask mk, int64_t T, int K, int H, int E,
                      SpecialArgs sp, Partials part) {
   constexpr int kB = batch_slots<kSharedAlpha>();
   __shared__ int s_ent[kWaves][kRoundSlots];
@@ -267,19 +268,21 @@ k_const_grad_partial(const uint16_t* __restrict__ grad_out, const int32_t* __res
     // all 16 loads first (slots past the segment read its last slot instead)
     int idv[8];
     float pp[8];
+    bool act[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int64_t s = base + j * kWave + lane;
       const int64_t sl = s < s_hi ? s : s_hi - 1;
       idv[j] = ids[sl];
       pp[j] = probs[sl];
+      act[j] = mk.active(sl);
     }
     int cq[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int64_t c = int64_t(idv[j]) - const_lo;
-      const bool ok = base + j * kWave + lane < s_hi && c >= c0 && c < c0 + kConstGroup &&
-                      c < sp.num_const;
+      const bool ok = base + j * kWave + lane < s_hi && act[j] && c >= c0 &&
+                      c < c0 + kConstGroup && c < sp.num_const;
       cq[j] = ok ? static_cast<int>(c - c0) : -1;
     }
     int count = 0;
@@ -534,9 +537,9 @@ size_t combine_grad_workspace_bytes(int64_t T, int H, int num_const) {
 
 hipError_t launch_combine_grad(const uint16_t* grad_out, const uint16_t* expert_out, int64_t N,
                                const int32_t* row_of_slot, const int32_t* row_map,
-                               const int32_t* ids, const float* probs, int64_t T, int K, int H,
-                               int E, const SpecialArgs& sp, const CombineGradArgs& o, void* ws,
-                               hipStream_t st) {
+                               const int32_t* ids, const float* probs, SlotMask mk, int64_t T,
+                               int K, int H, int E, const SpecialArgs& sp,
+                               const CombineGradArgs& o, void* ws, hipStream_t st) {
   if (T == 0) return hipGetLastError();
   const AlphaLayout lay = classify_alpha(sp, H);
   const bool want_alpha = o.d_alpha1 != nullptr || o.d_alpha2 != nullptr;
@@ -550,7 +553,8 @@ hipError_t launch_combine_grad(const uint16_t* grad_out, const uint16_t* expert_
     const dim3 block(kWaves * kWave);
 #define MOE_CGRAD(RM, PH, MK)                                                                  \
   hipLaunchKernelGGL((k_combine_grad<RM, PH, MK>), grid, block, 0, st, grad_out, expert_out, N, \
-                     row_of_slot, row_map, ids, probs, T, K, H, E, sp, o, alpha_token, nsplit)
+                     row_of_slot, row_map, ids, probs, mk, T, K, H, E, sp, o, alpha_token,    \
+                     nsplit)
 #define MOE_CGRAD_K(RM, PH) \
   if (K <= 8) MOE_CGRAD(RM, PH, 8); else MOE_CGRAD(RM, PH, 16);
     if (row_map != nullptr) {
@@ -576,7 +580,7 @@ hipError_t launch_combine_grad(const uint16_t* grad_out, const uint16_t* expert_
   const dim3 block(kWaves * kWave);
 #define MOE_CPART(PH, SA)                                                                       \
   hipLaunchKernelGGL((k_const_grad_partial<PH, SA>), grid, block, 0, st, grad_out, ids, probs, \
-                     T, K, H, E, sp, part)
+                     mk, T, K, H, E, sp, part)
   if (per_h) {
     if (shared_alpha) MOE_CPART(true, true); else MOE_CPART(true, false);
   } else {

@@ -8,8 +8,24 @@
 
 namespace moe {
 
+// x_active_mask: which slots take part in the exchange. m == nullptr: all of
+// them; per_slot: one flag per slot [T*K], else one per token [T]. A slot
+// that takes no part is treated as a dropped slot (no row, no term).
+struct SlotMask {
+  const uint8_t* m;
+  int per_slot;
+  int K;
+  __device__ __forceinline__ bool active(int64_t s) const {
+    if (m == nullptr) return true;
+    const uint32_t i = per_slot ? static_cast<uint32_t>(s)
+                                : static_cast<uint32_t>(s) / static_cast<uint32_t>(K);
+    return m[i] != 0;
+  }
+};
+
 size_t permute_workspace_bytes(int64_t T, int K, int E);
-hipError_t launch_permute(const uint16_t* x, const int32_t* ids, int64_t T, int H, int K, int E,
+hipError_t launch_permute(const uint16_t* x, const int32_t* ids, SlotMask mk, int64_t T, int H,
+                          int K, int E,
                           uint16_t* permuted, int32_t* sorted_slot, int32_t* row_of_slot,
                           int32_t* counts, int32_t* offsets, void* ws, hipStream_t st);
 
@@ -29,7 +45,7 @@ struct SpecialArgs {
 
 hipError_t launch_combine(const uint16_t* expert_out, int64_t N, const int32_t* row_of_slot,
                           const int32_t* row_map, const int32_t* ids, const float* probs,
-                          int64_t T, int K, int H, int E, const SpecialArgs& sp,
+                          SlotMask mk, int64_t T, int K, int H, int E, const SpecialArgs& sp,
                           const uint16_t* shared_x, uint16_t* out, hipStream_t st);
 
 // Outputs of the combine backward (every pointer but d_probs nullable).
@@ -52,9 +68,9 @@ AlphaLayout classify_alpha(const SpecialArgs& sp, int H);
 size_t combine_grad_workspace_bytes(int64_t T, int H, int num_const);
 hipError_t launch_combine_grad(const uint16_t* grad_out, const uint16_t* expert_out, int64_t N,
                                const int32_t* row_of_slot, const int32_t* row_map,
-                               const int32_t* ids, const float* probs, int64_t T, int K, int H,
-                               int E, const SpecialArgs& sp, const CombineGradArgs& o, void* ws,
-                               hipStream_t st);
+                               const int32_t* ids, const float* probs, SlotMask mk, int64_t T,
+                               int K, int H, int E, const SpecialArgs& sp,
+                               const CombineGradArgs& o, void* ws, hipStream_t st);
 
 hipError_t launch_permute_grad(const uint16_t* d_permuted, int64_t N, const int32_t* row_of_slot,
                                int64_t T, int K, int H, uint16_t* d_x, hipStream_t st);

@@ -63,7 +63,7 @@ constexpr int kBatch = 8;
 
 // Per-chunk histogram, chunk-major: hist[b * E + e] = #slots of chunk b with id e.
 __global__ void __launch_bounds__(kChunkThreads)
-k_route_count(const int32_t* __restrict__ ids, int64_t S, int E, int iters,
+k_route_count(const int32_t* __restrict__ ids, SlotMask mk, int64_t S, int E, int iters,
               int32_t* __restrict__ hist) {
   extern __shared__ int32_t cnt[];  // [E]
   for (int e = threadIdx.x; e < E; e += kChunkThreads) cnt[e] = 0;
@@ -72,14 +72,17 @@ k_route_count(const int32_t* __restrict__ ids, int64_t S, int E, int iters,
   const int64_t base = b * int64_t(kChunkThreads) * iters;
   for (int j0 = 0; j0 < iters; j0 += kBatch) {
     int id[kBatch];
+    bool act[kBatch];
 #pragma unroll
     for (int q = 0; q < kBatch; ++q) {
       const int64_t s = base + int64_t(j0 + q) * kChunkThreads + threadIdx.x;
-      id[q] = (j0 + q < iters && s < S) ? ids[s] : -1;
+      const bool in = j0 + q < iters && s < S;
+      id[q] = in ? ids[s] : -1;
+      act[q] = in && mk.active(s);
     }
 #pragma unroll
     for (int q = 0; q < kBatch; ++q)
-      if (id[q] >= 0 && id[q] < E) atomicAdd(&cnt[id[q]], 1);
+      if (act[q] && id[q] >= 0 && id[q] < E) atomicAdd(&cnt[id[q]], 1);
   }
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += kChunkThreads) hist[b * E + e] = cnt[e];
@@ -89,7 +92,8 @@ k_route_count(const int32_t* __restrict__ ids, int64_t S, int E, int iters,
 // of bucket e that belongs to this chunk: writes row_of_slot[s] and
 // sorted_slot[row], and -1 into sorted_slot rows [N, S) of the chunk's range.
 template <typename ChunkBase>
-__device__ void scatter_chunk(const int32_t* __restrict__ ids, int64_t S, int E, int iters,
+__device__ void scatter_chunk(const int32_t* __restrict__ ids, SlotMask mk, int64_t S, int E,
+                              int iters,
                               int64_t b, ChunkBase chunk_base, int32_t N, int32_t* run,
                               int32_t* __restrict__ sorted_slot, int32_t* __restrict__ row_of_slot) {
   const int w = threadIdx.x / kWave;
@@ -99,12 +103,18 @@ __device__ void scatter_chunk(const int32_t* __restrict__ ids, int64_t S, int E,
   const int64_t wbase = b * int64_t(kChunkThreads) * iters + int64_t(w) * kWave * iters;
   int32_t* my = run + w * E;
   // ids of slots wbase + (j0 + q) * 64 + lane, q < kBatch
+  // (slots outside the active mask read as id -1)
   auto load_batch = [&](int j0, int id[kBatch]) {
+    bool act[kBatch];
 #pragma unroll
     for (int q = 0; q < kBatch; ++q) {
       const int64_t s = wbase + int64_t(j0 + q) * kWave + lane;
-      id[q] = (j0 + q < iters && s < S) ? ids[s] : -1;
+      const bool in = j0 + q < iters && s < S;
+      id[q] = in ? ids[s] : -1;
+      act[q] = in && mk.active(s);
     }
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) id[q] = act[q] ? id[q] : -1;
   };
   // pass 1: per-wave counts
   for (int j0 = 0; j0 < iters; j0 += kBatch) {
@@ -160,7 +170,8 @@ __device__ void scatter_chunk(const int32_t* __restrict__ ids, int64_t S, int E,
 // table itself (per expert: all chunks, and the chunks before its own), scans
 // the expert totals in LDS, and chunk 0 publishes counts and offsets.
 __global__ void __launch_bounds__(kChunkThreads)
-k_route_scan_scatter(const int32_t* __restrict__ ids, int64_t S, int E, int iters, int64_t nblk,
+k_route_scan_scatter(const int32_t* __restrict__ ids, SlotMask mk, int64_t S, int E, int iters,
+                     int64_t nblk,
                      const int32_t* __restrict__ hist, int32_t* __restrict__ counts,
                      int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_slot,
                      int32_t* __restrict__ row_of_slot) {
@@ -214,7 +225,7 @@ k_route_scan_scatter(const int32_t* __restrict__ ids, int64_t S, int E, int iter
   if (b == 0 && threadIdx.x == 0) offsets[E] = N;
   __syncthreads();
   scatter_chunk(
-      ids, S, E, iters, b, [&](int e) { return off[e] + before[e]; }, N, run, sorted_slot,
+      ids, mk, S, E, iters, b, [&](int e) { return off[e] + before[e]; }, N, run, sorted_slot,
       row_of_slot);
 }
 
@@ -256,8 +267,8 @@ size_t permute_workspace_bytes(int64_t T, int K, int E) {
   return static_cast<size_t>(std::max<int64_t>(1, p.nblk) * E) * sizeof(int32_t);
 }
 
-hipError_t launch_permute(const uint16_t* x, const int32_t* ids, int64_t T, int H, int K, int E,
-                          uint16_t* permuted, int32_t* sorted_slot, int32_t* row_of_slot,
+hipError_t launch_permute(const uint16_t* x, const int32_t* ids, SlotMask mk, int64_t T, int H,
+                          int K, int E, uint16_t* permuted, int32_t* sorted_slot, int32_t* row_of_slot,
                           int32_t* counts, int32_t* offsets, void* ws, hipStream_t st) {
   const int64_t S = T * K;
   const PermutePlan p = plan_for(S, E);
@@ -267,10 +278,10 @@ hipError_t launch_permute(const uint16_t* x, const int32_t* ids, int64_t T, int 
     return hipGetLastError();
   }
   hipLaunchKernelGGL(k_route_count, dim3(static_cast<unsigned>(p.nblk)), dim3(kChunkThreads),
-                     E * sizeof(int32_t), st, ids, S, E, p.iters, table);
+                     E * sizeof(int32_t), st, ids, mk, S, E, p.iters, table);
   const size_t lds = (size_t(kChunkWaves) * E + 2 * E + kChunkThreads) * sizeof(int32_t);
   hipLaunchKernelGGL(k_route_scan_scatter, dim3(static_cast<unsigned>(p.nblk)),
-                     dim3(kChunkThreads), lds, st, ids, S, E, p.iters, p.nblk, table, counts,
+                     dim3(kChunkThreads), lds, st, ids, mk, S, E, p.iters, p.nblk, table, counts,
                      offsets, sorted_slot, row_of_slot);
   if (permuted != nullptr) {
     hipLaunchKernelGGL(k_permute_rows, dim3(static_cast<unsigned>(ceil_div(T, kRowWaves))),

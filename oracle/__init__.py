@@ -56,6 +56,13 @@ def _load():
                                      _i32, _i32, _i32, _i32, _i32, _u16p, _f32p, _f32p, _i64,
                                      _i64, _i64, _i64, _u16p, _f64p, _u8p, _f64p, _f64p, _f64p,
                                      _f64p, _f64p, _f64p]
+    _i64p = ctypes.POINTER(ctypes.c_int64)
+    for name in ("orc_dered_indices_loop", "orc_dered_indices_vectorized"):
+        getattr(lib, name).argtypes = [_i32p, _i32, _i32, _i32, _i32, _i32, _i64, _i32p, _i32p,
+                                       _i64p]
+        getattr(lib, name).restype = ctypes.c_int
+    lib.orc_scatter_add_rows.argtypes = [_u16p, _f32p, _i32p, _i64, _i32, _i64, _u16p, _f64p]
+    lib.orc_scatter_add_rows.restype = ctypes.c_int
     lib.orc_num_threads.argtypes = []
     for name in ("orc_permute", "orc_reorder_loop", "orc_reorder_index_vectorized",
                  "orc_swiglu_row", "orc_grouped_swiglu", "orc_combine", "orc_unpermute_grad",
@@ -323,3 +330,40 @@ def combine_grad(grad_out, expert_out, row_of_slot, expert_ids, probs, E: int, *
     _check(rc, "combine_grad")
     out["row_written"] = out["row_written"].astype(bool)
     return out
+
+
+# --------------------------------------------------------------------------- deredundency
+
+def dered_indices(counts_by_source, expert_start: int, iep_size: int, num_local: int, *,
+                  capacity: int | None = None, form: str = "loop"):
+    """Deredundency dispatch indices. Returns (indices [capacity] int32 with -1
+    past the total, counts_by_dest [iep_size*num_local], total)."""
+    c = _c(counts_by_source, np.int32)
+    oep, E = c.shape
+    if capacity is None:
+        capacity = int(np.maximum(c, 0).sum())
+    idx = np.empty(capacity, dtype=np.int32)
+    cbd = np.empty(iep_size * num_local, dtype=np.int32)
+    tot = ctypes.c_int64(0)
+    fn = {"loop": _load().orc_dered_indices_loop,
+          "vectorized": _load().orc_dered_indices_vectorized}[form]
+    rc = fn(_ptr(c, ctypes.c_int32), oep, E, expert_start, iep_size, num_local, capacity,
+            _ptr(idx, ctypes.c_int32), _ptr(cbd, ctypes.c_int32), ctypes.byref(tot))
+    _check(rc, "dered_indices")
+    return idx, cbd, int(tot.value)
+
+
+def scatter_add_rows(src, indices, G: int, coeff=None):
+    """whiteboard = zeros[G, H]; whiteboard[indices[j]] += coeff[j] * src[j].
+    Returns (bf16 bits [G, H], fp64 [G, H])."""
+    sr = _c(src, np.uint16)
+    n, H = sr.shape
+    ix = _c(indices, np.int32)
+    cf = _c(coeff, np.float32) if coeff is not None else None
+    out = np.empty((G, H), dtype=np.uint16)
+    out64 = np.empty((G, H), dtype=np.float64)
+    rc = _load().orc_scatter_add_rows(_ptr(sr, ctypes.c_uint16), _ptr(cf, ctypes.c_float),
+                                      _ptr(ix, ctypes.c_int32), n, H, G,
+                                      _ptr(out, ctypes.c_uint16), _ptr(out64, ctypes.c_double))
+    _check(rc, "scatter_add_rows")
+    return out, out64

@@ -357,6 +357,28 @@ def run_ops(args, dev, flush):
                                                    nbytes=permute_grad_bytes(T, K, H, N))))
     del dx
     del gout, perm5, dperm
+    # deredundency: dispatch indices and whiteboard combine of one outer step
+    g = W.gen_dered()
+    c = g["cfg"]
+    cnt = dt(g["counts"], dev)
+    n_sel, G, H = g["n_selected"], g["G"], c["H"]
+    di = moe.dered_indices_alloc(cnt, c["expert_start"], c["iep"], c["El"], capacity=n_sel)
+    wsi = moe.workspace(moe.moe_deredundency_dispatch_indices_workspace_size(
+        c["oep"], c["E"], c["iep"], c["El"]), dev)
+    f_di = lambda: moe.moe_deredundency_dispatch_indices(
+        cnt, c["oep"], c["E"], c["expert_start"], c["iep"], c["El"], n_sel, di["indices"],
+        di["counts_by_dest"], di["total"], wsi)
+    src, coeff = dbf(g["outer_output"], dev), dt(g["router_coeff"], dev)
+    wb = torch.empty((G, H), dtype=torch.bfloat16, device=dev)
+    wsc = moe.workspace(moe.moe_deredundency_combine_workspace_size(G), dev)
+    f_dc = lambda: moe.moe_deredundency_combine(src, coeff, di["indices"], n_sel, H, G, wb, wsc)
+    ops.append(dict(workload=c["name"], **op_entry(
+        "deredundency_dispatch_indices", *time_op(f_di, args.op_iters, flush),
+        nbytes=c["oep"] * c["E"] * 4 + n_sel * 4)))
+    ops.append(dict(workload=c["name"], **op_entry(
+        "deredundency_combine", *time_op(f_dc, args.op_iters, flush),
+        nbytes=n_sel * H * 2 + G * H * 2 + n_sel * 8 + G * 8)))
+    del src, wb
     # device-to-device copy of 1 GiB for reference
     a = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev)
     b = torch.empty_like(a)

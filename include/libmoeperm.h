@@ -68,6 +68,7 @@ int32_t moe_abi_version(void);
 /* Limits enforced by the host checks. */
 #define MOE_MAX_TOPK 16         /* [CV2] 约束说明: 0 < K <= 16 */
 #define MOE_MAX_EXPERTS 1024    /* [CV2] 参数说明 moe_expert_num: [1, 1024] */
+#define MOE_MAX_DERED_CELLS (1 << 22)  /* oep_size * num_experts of the deredundency count table */
 #define MOE_MAX_REORDER_BLOCKS 65536 /* R * E_local */
 
 /* ------------------------------------------------------------------------
@@ -322,6 +323,71 @@ moe_status_t moe_unpermute_grad(const void* grad_out, const void* permuted, int6
  * ------------------------------------------------------------------------ */
 moe_status_t moe_permute_grad(const void* d_permuted, int64_t N, const int32_t* row_of_slot,
                               int64_t T, int32_t K, int32_t H, void* d_x, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * moe_deredundency_dispatch_indices -- gather-view indices of one outer
+ * expert range, ordered [iep_dst, local_expert, oep_source].
+ *
+ * [EP] _generate_deredundency_dispatch_indices. tokens_per_expert_by_source
+ * [oep_size, num_experts] (device) describes each source rank's expert-major
+ * routed buffer; the buffers are concatenated in source order (the gathered
+ * buffer, G = sum of all counts rows). The selected experts are
+ * e = expert_start + d*num_local_experts + l for d < iep_size,
+ * l < num_local_experts; block (d, l, s) holds source s's rows of expert e, in
+ * their order, and blocks follow in (d, l, s) order. indices[i] is the
+ * gathered row of selected row i (int32 here: the page returns int64);
+ * positions past the total get -1. counts_by_dest[d*num_local_experts + l]
+ * sums expert e over the sources. Negative counts read as 0; the sum of all
+ * counts must stay below 2^31.
+ *
+ *  tokens_per_expert_by_source int32 [oep_size * num_experts] in   device
+ *  indices        int32 [capacity]                 out  -1 past the total
+ *  counts_by_dest int32 [iep_size * num_local_experts] out
+ *  total          int32 [1]                        out  (nullable) the number of selected rows
+ * Errors: INVALID_ARG for oep_size, num_experts, iep_size or num_local_experts
+ * < 1, expert_start < 0, expert_start + iep_size*num_local_experts >
+ * num_experts, oep_size*num_experts > MOE_MAX_DERED_CELLS, capacity outside
+ * [0, INT32_MAX], NULL / misaligned pointers; WORKSPACE if too small.
+ * ------------------------------------------------------------------------ */
+moe_status_t moe_deredundency_dispatch_indices_workspace_size(int32_t oep_size,
+                                                             int32_t num_experts,
+                                                             int32_t iep_size,
+                                                             int32_t num_local_experts,
+                                                             size_t* bytes);
+moe_status_t moe_deredundency_dispatch_indices(
+    const int32_t* tokens_per_expert_by_source, int32_t oep_size, int32_t num_experts,
+    int32_t expert_start, int32_t iep_size, int32_t num_local_experts, int64_t capacity,
+    int32_t* indices, int32_t* counts_by_dest, int32_t* total, void* workspace,
+    size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * moe_deredundency_combine -- the whiteboard of the deredundency combine.
+ *
+ * [EP] _scale_by_router_coeff then _scatter_add_first_dim: outer_output row j
+ * is scaled by router_coeff[j] and added into a zero [G, H] buffer at row
+ * dispatch_indices[j]:
+ *     whiteboard[r] = bf16( router_coeff[j] * outer_output[j] )  if dispatch_indices[j] == r
+ *                   = 0                                           if no j names r
+ * (the product correctly rounded; router_coeff NULL: the rows are copied).
+ * As in a zero buffer plus the row, an exactly zero product is +0.
+ * The dispatch indices of moe_deredundency_dispatch_indices name every row at
+ * most once, which this call requires: two j naming the same row leave one of
+ * the two scaled rows there, not their sum. Indices outside [0, G) are skipped.
+ * Every row of the whiteboard is written once (no separate zero fill).
+ *
+ *  outer_output     bf16 [n, H]  in
+ *  router_coeff     fp32 [n]     in  (nullable)
+ *  dispatch_indices int32 [n]    in
+ *  whiteboard       bf16 [G, H]  out
+ *  workspace        moe_deredundency_combine_workspace_size(G) bytes
+ * Errors: INVALID_ARG for n or G outside [0, INT32_MAX], H <= 0, NULL /
+ * misaligned pointers; UNSUPPORTED for H % 8 != 0; WORKSPACE if too small.
+ * ------------------------------------------------------------------------ */
+moe_status_t moe_deredundency_combine_workspace_size(int64_t G, size_t* bytes);
+moe_status_t moe_deredundency_combine(const void* outer_output, const float* router_coeff,
+                                      const int32_t* dispatch_indices, int64_t n, int32_t H,
+                                      int64_t G, void* whiteboard, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

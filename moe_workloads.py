@@ -27,7 +27,7 @@ __all__ = [
     "bf16_from_f32", "f32_from_bf16", "rng_for", "normal_bf16", "uniform_bf16",
     "route_topk", "make_routing", "make_tokens", "make_expert_weights",
     "make_rank_major_counts", "CONFIGS", "gen_c1", "gen_c2", "gen_c3", "gen_c4",
-    "gen_c5", "generate",
+    "gen_c5", "generate", "DERED", "gen_dered",
 ]
 
 
@@ -258,6 +258,33 @@ def gen_c5(with_rows: bool = True):
         rr = rng_for(c["seed"] * 1000 + 1)
         out["grad_out"] = normal_bf16(rr, (T, H))
         out["permuted"] = normal_bf16(rr, (T * K, H))
+    return out
+
+
+DERED = dict(name="deredundency_oep8_E256_H2048", oep=8, E=256, rows_per_source=8192, H=2048,
+             expert_start=0, iep=8, El=32, seed=6)
+
+
+def gen_dered(with_rows: bool = True):
+    """One outer step of the deredundency combine at the skewed layer's sizes:
+    8 source ranks, each with 1024 tokens x top-8 = 8192 routed rows over
+    256 experts drawn with the Zipf(1.2) popularity of the skewed layer
+    (counts[s] ~ Multinomial(8192, p), p_e proportional to rank_e^-1.2 with a
+    seeded rank permutation); the outer range takes all 256 experts as
+    8 destinations x 32 local experts. router_coeff ~ U(0, 1) per selected row,
+    outer_output bf16 N(0, 1)."""
+    c = DERED
+    rng = rng_for(c["seed"])
+    rank = rng.permutation(c["E"]) + 1
+    pv = rank.astype(np.float64) ** -1.2
+    pv /= pv.sum()
+    counts = np.stack([rng.multinomial(c["rows_per_source"], pv)
+                       for _ in range(c["oep"])]).astype(np.int32)
+    n = int(counts[:, c["expert_start"]:c["expert_start"] + c["iep"] * c["El"]].sum())
+    out = dict(cfg=c, counts=counts, n_selected=n, G=int(counts.sum()),
+               router_coeff=rng.uniform(0.0, 1.0, size=n).astype(np.float32))
+    if with_rows:
+        out["outer_output"] = normal_bf16(rng_for(c["seed"] * 1000 + 1), (n, c["H"]))
     return out
 
 

@@ -251,6 +251,38 @@ def test_combine_grad_checks(lib):
         b.moe_unpermute_combine_grad_workspace_size(-1, 64, 2)
 
 
+@no_gpu
+def test_dered_checks(lib):
+    def idx(c=P, oep=4, E=16, start=0, iep=2, El=4, cap=100, ind=P, cbd=P, tot=None, ws=P,
+            wsb=1 << 20):
+        return lib.moe_deredundency_dispatch_indices(c, oep, E, start, iep, El, cap, ind, cbd, tot,
+                                                     ws, wsb, None)
+
+    assert idx(oep=0) == INVALID
+    assert idx(start=-1) == INVALID
+    assert idx(start=9) == INVALID                     # 9 + 2*4 > 16
+    assert idx(iep=5) == INVALID                       # 5*4 > 16
+    assert idx(oep=1 << 20, E=16) == INVALID           # count table too large
+    assert idx(cap=-1) == INVALID
+    assert idx(c=None) == INVALID
+    assert idx(ind=PM) == INVALID
+    assert idx(tot=PM) == INVALID
+    assert idx(ws=None) == WORKSPACE
+    assert idx(wsb=8) == WORKSPACE
+
+    def comb(src=P, cf=None, ind=P, n=10, H=64, G=20, wb=P, ws=P, wsb=1 << 20):
+        return lib.moe_deredundency_combine(src, cf, ind, n, H, G, wb, ws, wsb, None)
+
+    assert comb(n=-1) == INVALID
+    assert comb(G=-1) == INVALID
+    assert comb(H=12) == UNSUPPORTED
+    assert comb(src=P + 8) == INVALID
+    assert comb(cf=PM) == INVALID
+    assert comb(wb=None) == INVALID
+    assert comb(ws=None) == WORKSPACE
+    assert comb(wsb=4) == WORKSPACE
+
+
 def test_binding_rejects_wrong_tensors(lib):
     from unpermute_combine_moe_amd import binding as b
 

@@ -48,6 +48,8 @@ EXPORTS = (
     "moe_grouped_gemm_swiglu_workspace_size", "moe_grouped_gemm_swiglu",
     "moe_unpermute_combine", "moe_unpermute_grad", "moe_permute_grad",
     "moe_unpermute_combine_grad_workspace_size", "moe_unpermute_combine_grad",
+    "moe_deredundency_dispatch_indices_workspace_size", "moe_deredundency_dispatch_indices",
+    "moe_deredundency_combine_workspace_size", "moe_deredundency_combine",
 )
 
 _lib = None
@@ -85,6 +87,12 @@ def load(path: str = LIB_PATH):
     lib.moe_unpermute_combine_grad.argtypes = [
         _vp, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32,
         ctypes.POINTER(MoeSpecialExperts), _vp, _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    lib.moe_deredundency_dispatch_indices_workspace_size.argtypes = [_i32, _i32, _i32, _i32, sz]
+    lib.moe_deredundency_dispatch_indices.argtypes = [_vp, _i32, _i32, _i32, _i32, _i32, _i64,
+                                                      _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+    lib.moe_deredundency_combine_workspace_size.argtypes = [_i64, sz]
+    lib.moe_deredundency_combine.argtypes = [_vp, _vp, _vp, _i64, _i32, _i64, _vp, _vp,
+                                             ctypes.c_size_t, _vp]
     for name in EXPORTS[2:]:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -260,6 +268,42 @@ def moe_unpermute_combine_grad(grad_out, expert_out, N, row_of_slot, row_map, ex
         "moe_unpermute_combine_grad")
 
 
+def moe_deredundency_dispatch_indices_workspace_size(oep_size, num_experts, iep_size,
+                                                     num_local_experts) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().moe_deredundency_dispatch_indices_workspace_size(
+        oep_size, num_experts, iep_size, num_local_experts, ctypes.byref(n)),
+        "moe_deredundency_dispatch_indices_workspace_size")
+    return n.value
+
+
+def moe_deredundency_dispatch_indices(tokens_per_expert_by_source, oep_size, num_experts,
+                                      expert_start, iep_size, num_local_experts, capacity, indices,
+                                      counts_by_dest, total, ws, stream=None):
+    _check(load().moe_deredundency_dispatch_indices(
+        _ptr(tokens_per_expert_by_source, _I32, "tokens_per_expert_by_source"), oep_size,
+        num_experts, expert_start, iep_size, num_local_experts, capacity,
+        _ptr(indices, _I32, "indices"), _ptr(counts_by_dest, _I32, "counts_by_dest"),
+        _ptr(total, _I32, "total"), _ptr(ws, None, "workspace"),
+        ws.numel() if ws is not None else 0, _stream(stream)), "moe_deredundency_dispatch_indices")
+
+
+def moe_deredundency_combine_workspace_size(G) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().moe_deredundency_combine_workspace_size(G, ctypes.byref(n)),
+           "moe_deredundency_combine_workspace_size")
+    return n.value
+
+
+def moe_deredundency_combine(outer_output, router_coeff, dispatch_indices, n, H, G, whiteboard, ws,
+                             stream=None):
+    _check(load().moe_deredundency_combine(
+        _ptr(outer_output, _BF16, "outer_output"), _ptr(router_coeff, _F32, "router_coeff"),
+        _ptr(dispatch_indices, _I32, "dispatch_indices"), n, H, G,
+        _ptr(whiteboard, _BF16, "whiteboard"), _ptr(ws, None, "workspace"),
+        ws.numel() if ws is not None else 0, _stream(stream)), "moe_deredundency_combine")
+
+
 # --------------------------------------------------------------------------- allocating helpers
 
 def permute_alloc(x, expert_ids, num_experts, *, rows: bool = True, active_mask=None, stream=None):
@@ -372,3 +416,30 @@ def combine_grad_alloc(grad_out, expert_out, row_of_slot, expert_ids, probs, num
                                r.get("d_ori_x"), r.get("d_alpha1"), r.get("d_alpha2"),
                                r.get("d_const_v"), ws, stream, active_mask=active_mask)
     return r
+
+
+def dered_indices_alloc(tokens_per_expert_by_source, expert_start, iep_size, num_local_experts, *,
+                        capacity=None, stream=None):
+    """Returns dict(indices [capacity], counts_by_dest, total [1]); capacity
+    defaults to the number of gathered rows (no host read of the counts)."""
+    oep, E = tokens_per_expert_by_source.shape
+    dev = tokens_per_expert_by_source.device
+    if capacity is None:
+        raise ValueError("capacity: give the row capacity of the indices buffer")
+    out = dict(indices=torch.empty(capacity, dtype=_I32, device=dev),
+               counts_by_dest=torch.empty(iep_size * num_local_experts, dtype=_I32, device=dev),
+               total=torch.empty(1, dtype=_I32, device=dev))
+    ws = workspace(moe_deredundency_dispatch_indices_workspace_size(oep, E, iep_size,
+                                                                    num_local_experts), dev)
+    moe_deredundency_dispatch_indices(tokens_per_expert_by_source, oep, E, expert_start, iep_size,
+                                      num_local_experts, capacity, out["indices"],
+                                      out["counts_by_dest"], out["total"], ws, stream)
+    return out
+
+
+def dered_combine_alloc(outer_output, router_coeff, dispatch_indices, G, *, stream=None):
+    n, H = outer_output.shape
+    wb = torch.empty((G, H), dtype=_BF16, device=outer_output.device)
+    ws = workspace(moe_deredundency_combine_workspace_size(G), outer_output.device)
+    moe_deredundency_combine(outer_output, router_coeff, dispatch_indices, n, H, G, wb, ws, stream)
+    return wb

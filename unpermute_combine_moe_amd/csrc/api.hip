@@ -313,3 +313,74 @@ MOE_API moe_status_t moe_unpermute_grad(const void* grad_out, const void* permut
   return hip_status(moe::launch_unpermute_grad(u16(grad_out), u16(permuted), N, row_of_slot,
                                                probs, T, K, H, u16(d_permuted), d_probs, stream));
 }
+
+// --------------------------------------------------------------------------- deredundency
+
+namespace {
+
+moe_status_t check_dered(int32_t oep, int32_t E, int32_t expert_start, int32_t iep, int32_t El) {
+  if (oep < 1 || E < 1 || iep < 1 || El < 1 || expert_start < 0) return MOE_ERR_INVALID_ARG;
+  if (int64_t(oep) * E > MOE_MAX_DERED_CELLS) return MOE_ERR_INVALID_ARG;
+  if (int64_t(iep) * El > E || int64_t(expert_start) + int64_t(iep) * El > E)
+    return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+}  // namespace
+
+MOE_API moe_status_t moe_deredundency_dispatch_indices_workspace_size(int32_t oep_size,
+                                                                      int32_t num_experts,
+                                                                      int32_t iep_size,
+                                                                      int32_t num_local_experts,
+                                                                      size_t* bytes) {
+  if (bytes == nullptr) return MOE_ERR_INVALID_ARG;
+  if (moe_status_t s = check_dered(oep_size, num_experts, 0, iep_size, num_local_experts))
+    return s;
+  *bytes = moe::dered_indices_workspace_bytes(oep_size, num_experts, iep_size, num_local_experts);
+  return MOE_OK;
+}
+
+MOE_API moe_status_t moe_deredundency_dispatch_indices(
+    const int32_t* tokens_per_expert_by_source, int32_t oep_size, int32_t num_experts,
+    int32_t expert_start, int32_t iep_size, int32_t num_local_experts, int64_t capacity,
+    int32_t* indices, int32_t* counts_by_dest, int32_t* total, void* workspace,
+    size_t workspace_bytes, hipStream_t stream) {
+  if (moe_status_t s =
+          check_dered(oep_size, num_experts, expert_start, iep_size, num_local_experts))
+    return s;
+  if (capacity < 0 || capacity > INT32_MAX) return MOE_ERR_INVALID_ARG;
+  if (!word_ok(tokens_per_expert_by_source) || !word_ok(counts_by_dest))
+    return MOE_ERR_INVALID_ARG;
+  if (capacity > 0 && !word_ok(indices)) return MOE_ERR_INVALID_ARG;
+  if (total != nullptr && !aligned(total, 4)) return MOE_ERR_INVALID_ARG;
+  const size_t need =
+      moe::dered_indices_workspace_bytes(oep_size, num_experts, iep_size, num_local_experts);
+  if (workspace == nullptr || !aligned(workspace, 4) || workspace_bytes < need)
+    return MOE_ERR_WORKSPACE;
+  return hip_status(moe::launch_dered_indices(tokens_per_expert_by_source, oep_size, num_experts,
+                                              expert_start, iep_size, num_local_experts, capacity,
+                                              indices, counts_by_dest, total, workspace, stream));
+}
+
+MOE_API moe_status_t moe_deredundency_combine_workspace_size(int64_t G, size_t* bytes) {
+  if (bytes == nullptr || G < 0 || G > INT32_MAX) return MOE_ERR_INVALID_ARG;
+  *bytes = moe::dered_combine_workspace_bytes(G);
+  return MOE_OK;
+}
+
+MOE_API moe_status_t moe_deredundency_combine(const void* outer_output, const float* router_coeff,
+                                              const int32_t* dispatch_indices, int64_t n,
+                                              int32_t H, int64_t G, void* whiteboard,
+                                              void* workspace, size_t workspace_bytes,
+                                              hipStream_t stream) {
+  if (n < 0 || n > INT32_MAX || G < 0 || G > INT32_MAX) return MOE_ERR_INVALID_ARG;
+  if (moe_status_t s = check_h(H)) return s;
+  if (n > 0 && (!row_ok(outer_output) || !word_ok(dispatch_indices))) return MOE_ERR_INVALID_ARG;
+  if (router_coeff != nullptr && !aligned(router_coeff, 4)) return MOE_ERR_INVALID_ARG;
+  if (G > 0 && !row_ok(whiteboard)) return MOE_ERR_INVALID_ARG;
+  if (G > 0 && (workspace == nullptr || !aligned(workspace, 4) ||
+                workspace_bytes < moe::dered_combine_workspace_bytes(G)))
+    return MOE_ERR_WORKSPACE;
+  return hip_status(moe::launch_dered_combine(u16(outer_output), router_coeff, dispatch_indices, n,
+                                              H, G, u16(whiteboard), workspace, stream));
+}

@@ -114,4 +114,36 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __host__ __device__ constexpr int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Exclusive scan of in[0..L) into out[0..L) by one workgroup of kThreads
+// threads (each a contiguous run, then a Hillis-Steele scan of the run sums in
+// part[kThreads], shared); returns the total to every thread. in and out may
+// alias. Every thread of the workgroup must call it.
+template <int kThreads>
+__device__ int32_t block_exclusive_scan(const int32_t* in, int32_t* out, int64_t L,
+                                        int32_t* part) {
+  const int64_t seg = ceil_div(L, kThreads);
+  const int64_t lo = std::min<int64_t>(L, threadIdx.x * seg);
+  const int64_t hi = std::min<int64_t>(L, lo + seg);
+  int32_t sum = 0;
+  for (int64_t i = lo; i < hi; ++i) sum += in[i];
+  __syncthreads();
+  part[threadIdx.x] = sum;
+  __syncthreads();
+  for (int off = 1; off < kThreads; off <<= 1) {
+    const int32_t v = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
+    __syncthreads();
+    part[threadIdx.x] += v;
+    __syncthreads();
+  }
+  int32_t run = part[threadIdx.x] - sum;
+  const int32_t total = part[kThreads - 1];
+  for (int64_t i = lo; i < hi; ++i) {
+    const int32_t c = in[i];
+    out[i] = run;
+    run += c;
+  }
+  __syncthreads();
+  return total;
+}
+
 }  // namespace moe

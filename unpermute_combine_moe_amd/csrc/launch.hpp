@@ -79,6 +79,16 @@ hipError_t launch_unpermute_grad(const uint16_t* grad_out, const uint16_t* permu
                                  const int32_t* row_of_slot, const float* probs, int64_t T, int K,
                                  int H, uint16_t* d_permuted, float* d_probs, hipStream_t st);
 
+size_t dered_indices_workspace_bytes(int oep, int E, int iep, int El);
+hipError_t launch_dered_indices(const int32_t* counts, int oep, int E, int expert_start, int iep,
+                                int El, int64_t capacity, int32_t* indices,
+                                int32_t* counts_by_dest, int32_t* total, void* ws,
+                                hipStream_t st);
+size_t dered_combine_workspace_bytes(int64_t G);
+hipError_t launch_dered_combine(const uint16_t* src, const float* coeff, const int32_t* indices,
+                                int64_t n, int H, int64_t G, uint16_t* wb, void* ws,
+                                hipStream_t st);
+
 size_t gemm_workspace_bytes(int E, int64_t N_cap, int H, int I);
 hipError_t launch_grouped_gemm_swiglu(const uint16_t* x, const int32_t* offsets, int E,
                                       int64_t N_cap, int H, int I, const uint16_t* wg,

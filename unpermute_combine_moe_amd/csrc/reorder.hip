@@ -20,35 +20,6 @@ constexpr int kSetupThreads = 1024;
 constexpr int kRowsPerWg = 32;
 constexpr int kRowThreads = 256;
 
-// Exclusive scan of in[0..L) into out[0..L) by one workgroup of kSetupThreads;
-// returns the total to every thread. in and out may alias.
-__device__ int32_t block_exclusive_scan(const int32_t* in, int32_t* out, int64_t L,
-                                        int32_t* part /* [kSetupThreads] shared */) {
-  const int64_t seg = ceil_div(L, kSetupThreads);
-  const int64_t lo = std::min<int64_t>(L, threadIdx.x * seg);
-  const int64_t hi = std::min<int64_t>(L, lo + seg);
-  int32_t sum = 0;
-  for (int64_t i = lo; i < hi; ++i) sum += in[i];
-  __syncthreads();
-  part[threadIdx.x] = sum;
-  __syncthreads();
-  for (int off = 1; off < kSetupThreads; off <<= 1) {
-    const int32_t v = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
-    __syncthreads();
-    part[threadIdx.x] += v;
-    __syncthreads();
-  }
-  int32_t run = part[threadIdx.x] - sum;
-  const int32_t total = part[kSetupThreads - 1];
-  for (int64_t i = lo; i < hi; ++i) {
-    const int32_t c = in[i];
-    out[i] = run;
-    run += c;
-  }
-  __syncthreads();
-  return total;
-}
-
 // ws layout (int32): src_rm[B] | cnt_em[B] | src_em[B] | dst_em[B] | total[1]
 __global__ void __launch_bounds__(kSetupThreads)
 k_reorder_setup(const int32_t* __restrict__ counts, int R, int El, int32_t* __restrict__ ws,
@@ -68,13 +39,13 @@ k_reorder_setup(const int32_t* __restrict__ counts, int R, int El, int32_t* __re
   }
   __syncthreads();
   // starts of the blocks in the rank-major source buffer
-  block_exclusive_scan(src_rm, src_rm, B, part);
+  block_exclusive_scan<kSetupThreads>(src_rm, src_rm, B, part);
   for (int i = threadIdx.x; i < B; i += kSetupThreads) {
     const int e = i / R, r = i % R;
     src_em[i] = src_rm[r * El + e];
   }
   // starts of the blocks in the expert-major destination buffer
-  const int32_t total = block_exclusive_scan(cnt_em, dst_em, B, part);
+  const int32_t total = block_exclusive_scan<kSetupThreads>(cnt_em, dst_em, B, part);
   for (int e = threadIdx.x; e < El; e += kSetupThreads) {
     const int32_t start = dst_em[e * R];
     const int32_t end = (e + 1 < El) ? dst_em[(e + 1) * R] : total;

@@ -63,6 +63,10 @@ def _load():
         getattr(lib, name).restype = ctypes.c_int
     lib.orc_scatter_add_rows.argtypes = [_u16p, _f32p, _i32p, _i64, _i32, _i64, _u16p, _f64p]
     lib.orc_scatter_add_rows.restype = ctypes.c_int
+    lib.orc_grouped_swiglu_grad.argtypes = [_u16p, _i32p, _i32, _i64, _i32, _i32, _u16p, _u16p,
+                                            _u16p, _u16p, _f64p, _f64p, _f64p, _f64p, _f64p,
+                                            _f64p, _f64p]
+    lib.orc_grouped_swiglu_grad.restype = ctypes.c_int
     lib.orc_num_threads.argtypes = []
     for name in ("orc_permute", "orc_reorder_loop", "orc_reorder_index_vectorized",
                  "orc_swiglu_row", "orc_grouped_swiglu", "orc_combine", "orc_unpermute_grad",
@@ -213,6 +217,27 @@ def grouped_swiglu(x, expert_offsets, w_gate, w_up, w_down, *, want_h: bool = Tr
                                     _ptr(y, ctypes.c_double))
     _check(rc, "grouped_swiglu")
     return h, y
+
+
+def grouped_swiglu_grad(x, expert_offsets, w_gate, w_up, w_down, dy):
+    """fp64 backward of grouped_swiglu. Returns dict(dx [N,H], dwg, dwu [E,H,I],
+    dwd [E,I,H], dh, dg, du [N,I])."""
+    xx = _c(x, np.uint16)
+    off = _c(expert_offsets, np.int32)
+    wg, wu, wd = _c(w_gate, np.uint16), _c(w_up, np.uint16), _c(w_down, np.uint16)
+    g = _c(dy, np.uint16)
+    E, H, I = wg.shape
+    N = xx.shape[0]
+    r = dict(dx=np.zeros((N, H)), dwg=np.zeros((E, H, I)), dwu=np.zeros((E, H, I)),
+             dwd=np.zeros((E, I, H)), dh=np.zeros((N, I)), dg=np.zeros((N, I)),
+             du=np.zeros((N, I)))
+    rc = _load().orc_grouped_swiglu_grad(
+        _ptr(xx, ctypes.c_uint16), _ptr(off, ctypes.c_int32), E, N, H, I,
+        _ptr(wg, ctypes.c_uint16), _ptr(wu, ctypes.c_uint16), _ptr(wd, ctypes.c_uint16),
+        _ptr(g, ctypes.c_uint16), *(_ptr(r[k], ctypes.c_double)
+                                    for k in ("dx", "dwg", "dwu", "dwd", "dh", "dg", "du")))
+    _check(rc, "grouped_swiglu_grad")
+    return r
 
 
 # --------------------------------------------------------------------------- combine

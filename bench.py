@@ -224,6 +224,30 @@ def step_calls(d):
     return permute, gemm, combine, grad
 
 
+def gemm_grad_op(args, d, n_rows):
+    """The grouped GEMM backward on the layer's own tensors: dy is the unpermute
+    backward's d_permuted, h the forward's. FLOPs counted: 12 N H I (dh, dx and
+    the three weight gradients; the gate/up recompute, 4 N H I more, is not)."""
+    import torch
+    import unpermute_combine_moe_amd as moe
+
+    c = d["cfg"]
+    T, H, E, K, I = c["T"], c["H"], c["E"], c["K"], c["I"]
+    S = T * K
+    bf = torch.bfloat16
+    dev = d["x"].device
+    dx = torch.empty((S, H), dtype=bf, device=dev)
+    dwg = torch.empty((E, H, I), dtype=bf, device=dev)
+    dwu = torch.empty((E, H, I), dtype=bf, device=dev)
+    dwd = torch.empty((E, I, H), dtype=bf, device=dev)
+    ws = moe.workspace(moe.moe_grouped_gemm_swiglu_grad_workspace_size(E, S, H, I), dev)
+    f = lambda: moe.moe_grouped_gemm_swiglu_grad(d["permuted"], d["offsets"], E, S, H, I, d["wg"],
+                                                 d["wu"], d["wd"], d["h"], d["d_perm"], dx, dwg,
+                                                 dwu, dwd, ws)
+    us, usmin = time_op(f, args.op_iters, None)
+    return op_entry("grouped_gemm_swiglu_grad", us, usmin, flops=12 * n_rows * H * I)
+
+
 def run_layer(args, dev):
     import torch
 
@@ -476,6 +500,7 @@ def main():
     ]
     ops = layer_ops
     if not args.no_ops:
+        ops.append(dict(workload=c["name"], **gemm_grad_op(args, d, n_rows)))
         flush = Flusher(dev)
         ops = ops + run_ops(args, dev, flush)
         del flush

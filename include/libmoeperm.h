@@ -170,6 +170,41 @@ moe_status_t moe_grouped_gemm_swiglu(const void* x, const int32_t* expert_offset
                                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * moe_grouped_gemm_swiglu_grad -- backward of moe_grouped_gemm_swiglu.
+ *
+ * [GMM] (the grouped matmul + swiglu of the forward, differentiated for
+ * training). For each expert e and row n of its group, with dy = dL/dy:
+ *     dh = dy . w_down[e]^T            g, u recomputed from x (fp32, not stored)
+ *     s = 1 / (1 + exp(-g)),  dg = dh * u * s * (1 + g * (1 - s)),  du = dh * g * s
+ *     dx[n] = dg . w_gate[e]^T + du . w_up[e]^T
+ *     dw_gate[e] = sum_n x[n]^T dg,  dw_up[e] = sum_n x[n]^T du,
+ *     dw_down[e] = sum_n h[n]^T dy[n]
+ * bf16 MFMA with fp32 accumulation; dh and [dg | du] are kept in the
+ * workspace as bf16; h is the forward's output (as stored). Experts without
+ * rows get zero weight gradients; rows of dx past expert_offsets[E] are not
+ * written.
+ *
+ *  x, expert_offsets, w_gate, w_up, w_down   as for moe_grouped_gemm_swiglu
+ *  h        bf16 [N_cap, I]   in  the forward's h
+ *  dy       bf16 [N_cap, H]   in
+ *  dx       bf16 [N_cap, H]   out
+ *  dw_gate, dw_up  bf16 [E, H, I]   out
+ *  dw_down         bf16 [E, I, H]   out
+ *  workspace  moe_grouped_gemm_swiglu_grad_workspace_size bytes, 256-byte
+ *             aligned (about 6 * N_cap * I bytes: dh and [dg | du])
+ * Errors: as moe_grouped_gemm_swiglu (INVALID_ARG, UNSUPPORTED unless
+ * H % 64 == 0 and I % 64 == 0, WORKSPACE).
+ * ------------------------------------------------------------------------ */
+moe_status_t moe_grouped_gemm_swiglu_grad_workspace_size(int32_t E, int64_t N_cap, int32_t H,
+                                                         int32_t I, size_t* bytes);
+moe_status_t moe_grouped_gemm_swiglu_grad(const void* x, const int32_t* expert_offsets, int32_t E,
+                                          int64_t N_cap, int32_t H, int32_t I, const void* w_gate,
+                                          const void* w_up, const void* w_down, const void* h,
+                                          const void* dy, void* dx, void* dw_gate, void* dw_up,
+                                          void* dw_down, void* workspace, size_t workspace_bytes,
+                                          hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * moe_unpermute_combine -- weighted top-K combine back to token order.
  *
  * [CV2] 计算公式: x = Sum(expert_scales * expert_out + shared_expert_x), with

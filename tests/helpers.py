@@ -70,3 +70,23 @@ def assert_h_within_ulp(h_bits: np.ndarray, h_ref: np.ndarray, what: str = "h"):
     bound = 2.0 ** -8 * np.abs(h_ref) + 1e-4 * rms
     bad = err > bound
     assert not bad.any(), f"{what}: {int(bad.sum())} elements beyond one bf16 ulp; worst {err.max():.3e}"
+
+
+BF16_U = 2.0 ** -8   # unit roundoff of bf16 (8-bit significand, round to nearest)
+
+
+def assert_dot_bound(got, ref, terms, what="", term_units=4, out_units=2):
+    """Elementwise error bound of a sum of products whose inputs went through
+    bf16: |got - ref| <= term_units * u * T + out_units * u * |ref|, with T the
+    sum of the magnitudes of the exact terms and u = 2^-8. Two roundings of an
+    input term (an intermediate stored as bf16 from a bf16-rounded operand)
+    cost at most 2u * T, the bf16 output u * |ref|; the bound doubles both."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape == np.shape(terms), (got.shape, ref.shape, np.shape(terms))
+    bound = term_units * BF16_U * np.asarray(terms) + out_units * BF16_U * np.abs(ref)
+    err = np.abs(got - ref)
+    bad = err > bound
+    assert not bad.any(), (f"{what}: {int(bad.sum())} of {ref.size} elements outside the bf16 "
+                           f"dot-product bound; worst err/bound {float(np.max(err / (bound + 1e-300))):.3f}")
+    return float(np.max(err / (bound + 1e-300))) if ref.size else 0.0

@@ -1,5 +1,5 @@
 """MI355X-native MoE expert hot path: token permute, rank-major -> expert-major
-reorder, grouped SwiGLU GEMM (bf16 MFMA), weighted unpermute-combine with
+reorder, grouped SwiGLU GEMM (bf16 MFMA) and its backward, weighted unpermute-combine with
 special experts, the backward of the permute and of the combine, and the
 deredundency dispatch indices and whiteboard combine.
 
@@ -16,7 +16,8 @@ from .binding import (  # noqa: F401
     moe_unpermute_combine_grad, moe_unpermute_combine_grad_workspace_size,
     moe_deredundency_dispatch_indices, moe_deredundency_dispatch_indices_workspace_size,
     moe_deredundency_combine, moe_deredundency_combine_workspace_size, dered_indices_alloc,
-    dered_combine_alloc,
+    dered_combine_alloc, moe_grouped_gemm_swiglu_grad, moe_grouped_gemm_swiglu_grad_workspace_size,
+    grouped_gemm_grad_alloc,
     moe_permute_grad, permute_alloc, permute_grad_alloc, reorder_alloc, status_str,
     unpermute_grad_alloc, workspace,
 )

@@ -50,6 +50,7 @@ EXPORTS = (
     "moe_unpermute_combine_grad_workspace_size", "moe_unpermute_combine_grad",
     "moe_deredundency_dispatch_indices_workspace_size", "moe_deredundency_dispatch_indices",
     "moe_deredundency_combine_workspace_size", "moe_deredundency_combine",
+    "moe_grouped_gemm_swiglu_grad_workspace_size", "moe_grouped_gemm_swiglu_grad",
 )
 
 _lib = None
@@ -93,6 +94,10 @@ def load(path: str = LIB_PATH):
     lib.moe_deredundency_combine_workspace_size.argtypes = [_i64, sz]
     lib.moe_deredundency_combine.argtypes = [_vp, _vp, _vp, _i64, _i32, _i64, _vp, _vp,
                                              ctypes.c_size_t, _vp]
+    lib.moe_grouped_gemm_swiglu_grad_workspace_size.argtypes = [_i32, _i64, _i32, _i32, sz]
+    lib.moe_grouped_gemm_swiglu_grad.argtypes = [_vp, _vp, _i32, _i64, _i32, _i32, _vp, _vp, _vp,
+                                                 _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                 ctypes.c_size_t, _vp]
     for name in EXPORTS[2:]:
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -304,6 +309,24 @@ def moe_deredundency_combine(outer_output, router_coeff, dispatch_indices, n, H,
         ws.numel() if ws is not None else 0, _stream(stream)), "moe_deredundency_combine")
 
 
+def moe_grouped_gemm_swiglu_grad_workspace_size(E, N_cap, H, I) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().moe_grouped_gemm_swiglu_grad_workspace_size(E, N_cap, H, I, ctypes.byref(n)),
+           "moe_grouped_gemm_swiglu_grad_workspace_size")
+    return n.value
+
+
+def moe_grouped_gemm_swiglu_grad(x, expert_offsets, E, N_cap, H, I, w_gate, w_up, w_down, h, dy,
+                                 dx, dw_gate, dw_up, dw_down, ws, stream=None):
+    _check(load().moe_grouped_gemm_swiglu_grad(
+        _ptr(x, _BF16, "x"), _ptr(expert_offsets, _I32, "expert_offsets"), E, N_cap, H, I,
+        _ptr(w_gate, _BF16, "w_gate"), _ptr(w_up, _BF16, "w_up"), _ptr(w_down, _BF16, "w_down"),
+        _ptr(h, _BF16, "h"), _ptr(dy, _BF16, "dy"), _ptr(dx, _BF16, "dx"),
+        _ptr(dw_gate, _BF16, "dw_gate"), _ptr(dw_up, _BF16, "dw_up"),
+        _ptr(dw_down, _BF16, "dw_down"), _ptr(ws, None, "workspace"),
+        ws.numel() if ws is not None else 0, _stream(stream)), "moe_grouped_gemm_swiglu_grad")
+
+
 # --------------------------------------------------------------------------- allocating helpers
 
 def permute_alloc(x, expert_ids, num_experts, *, rows: bool = True, active_mask=None, stream=None):
@@ -443,3 +466,19 @@ def dered_combine_alloc(outer_output, router_coeff, dispatch_indices, G, *, stre
     ws = workspace(moe_deredundency_combine_workspace_size(G), outer_output.device)
     moe_deredundency_combine(outer_output, router_coeff, dispatch_indices, n, H, G, wb, ws, stream)
     return wb
+
+
+def grouped_gemm_grad_alloc(x, expert_offsets, w_gate, w_up, w_down, h, dy, *, stream=None):
+    """Backward of the grouped SwiGLU FFN. Returns dict(dx, dw_gate, dw_up, dw_down)."""
+    E, H, I = w_gate.shape
+    N_cap = x.shape[0]
+    dev = x.device
+    out = dict(dx=torch.zeros((N_cap, H), dtype=_BF16, device=dev),
+               dw_gate=torch.empty((E, H, I), dtype=_BF16, device=dev),
+               dw_up=torch.empty((E, H, I), dtype=_BF16, device=dev),
+               dw_down=torch.empty((E, I, H), dtype=_BF16, device=dev))
+    ws = workspace(moe_grouped_gemm_swiglu_grad_workspace_size(E, N_cap, H, I), dev)
+    moe_grouped_gemm_swiglu_grad(x, expert_offsets, E, N_cap, H, I, w_gate, w_up, w_down, h, dy,
+                                 out["dx"], out["dw_gate"], out["dw_up"], out["dw_down"], ws,
+                                 stream)
+    return out

@@ -201,6 +201,38 @@ MOE_API moe_status_t moe_grouped_gemm_swiglu(const void* x, const int32_t* exper
                                                     u16(y), workspace, stream));
 }
 
+MOE_API moe_status_t moe_grouped_gemm_swiglu_grad_workspace_size(int32_t E, int64_t N_cap,
+                                                                 int32_t H, int32_t I,
+                                                                 size_t* bytes) {
+  if (bytes == nullptr) return MOE_ERR_INVALID_ARG;
+  if (E < 1 || E > MOE_MAX_EXPERTS || N_cap < 0 || N_cap > INT32_MAX || H <= 0 || I <= 0)
+    return MOE_ERR_INVALID_ARG;
+  if (H % 64 != 0 || I % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  *bytes = moe::gemm_grad_workspace_bytes(E, N_cap, H, I);
+  return MOE_OK;
+}
+
+MOE_API moe_status_t moe_grouped_gemm_swiglu_grad(
+    const void* x, const int32_t* expert_offsets, int32_t E, int64_t N_cap, int32_t H, int32_t I,
+    const void* w_gate, const void* w_up, const void* w_down, const void* h, const void* dy,
+    void* dx, void* dw_gate, void* dw_up, void* dw_down, void* workspace, size_t workspace_bytes,
+    hipStream_t stream) {
+  if (E < 1 || E > MOE_MAX_EXPERTS || N_cap < 0 || N_cap > INT32_MAX || H <= 0 || I <= 0)
+    return MOE_ERR_INVALID_ARG;
+  if (H % 64 != 0 || I % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  if (!word_ok(expert_offsets) || !row_ok(w_gate) || !row_ok(w_up) || !row_ok(w_down) ||
+      !row_ok(dw_gate) || !row_ok(dw_up) || !row_ok(dw_down))
+    return MOE_ERR_INVALID_ARG;
+  if (N_cap > 0 && (!row_ok(x) || !row_ok(h) || !row_ok(dy) || !row_ok(dx)))
+    return MOE_ERR_INVALID_ARG;
+  if (workspace == nullptr || !aligned(workspace, 256) ||
+      workspace_bytes < moe::gemm_grad_workspace_bytes(E, N_cap, H, I))
+    return MOE_ERR_WORKSPACE;
+  return hip_status(moe::launch_grouped_gemm_swiglu_grad(
+      u16(x), expert_offsets, E, N_cap, H, I, u16(w_gate), u16(w_up), u16(w_down), u16(h), u16(dy),
+      u16(dx), u16(dw_gate), u16(dw_up), u16(dw_down), workspace, stream));
+}
+
 // --------------------------------------------------------------------------- combine
 
 MOE_API moe_status_t moe_unpermute_combine(const void* expert_out, int64_t N,

@@ -130,7 +130,7 @@ __device__ int32_t block_exclusive_scan(const int32_t* in, int32_t* out, int64_t
   part[threadIdx.x] = sum;
   __syncthreads();
   for (int off = 1; off < kThreads; off <<= 1) {
-    const int32_t v = threadIdx.x >= off ? part[threadIdx.x - off] : 0;
+    const int32_t v = static_cast<int>(threadIdx.x) >= off ? part[threadIdx.x - off] : 0;
     __syncthreads();
     part[threadIdx.x] += v;
     __syncthreads();

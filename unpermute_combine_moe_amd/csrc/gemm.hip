@@ -102,10 +102,11 @@ constexpr int kLoadsB = kChunksB / kThreads;
 constexpr int kLoadsPerStage = kLoadsA + kLoadsB;
 constexpr int kStageBytes = (kChunksA + kChunksB) * 16;
 // epilogue stores per wave per tile: 2 row fragments x output fragments x 4
+// (x 2 in mode 2, which writes dg and du)
 template <int kMode>
 struct EpiloguePlan {
-  static constexpr int kOutFrags = (kMode == 0) ? 2 : 4;
-  static constexpr int kStores = 2 * kOutFrags * 4;
+  static constexpr int kOutFrags = (kMode == 1) ? 4 : 2;
+  static constexpr int kStores = 2 * kOutFrags * 4 * (kMode == 2 ? 2 : 1);
 };
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
@@ -148,11 +149,14 @@ __device__ __forceinline__ bf16x8_t lds_read_a(const lds_u8_t* base, int slot) {
 }
 
 // kMode 0: gate/up + SwiGLU -> h.  kMode 1: down -> y.
+// kMode 2: gate/up recomputed for the backward; with dh = aux [N, Ncols], the
+// epilogue writes C [N, 2 * Ncols] = [dg | du], dg = dh * u * s (1 + g (1 - s)),
+// du = dh * g * s, s = 1 / (1 + exp(-g)) (the SwiGLU derivative).
 template <int kMode>
 __global__ void __launch_bounds__(kThreads, 1)
 k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0,
        const uint16_t* __restrict__ B1, int Ncols, const int32_t* __restrict__ ws, int E,
-       uint16_t* __restrict__ C, uint2* __restrict__ trash) {
+       uint16_t* __restrict__ C, uint2* __restrict__ trash, const uint16_t* __restrict__ aux) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes];
   // row-tile prefix and clamped expert offsets, staged once per workgroup so the
   // per-tile expert lookup is a binary search in LDS
@@ -172,7 +176,7 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
   const int wm = wave & 1;   // 64-row half of the tile
   const int wn = wave >> 1;  // B-column half
 
-  constexpr int kOutCols = (kMode == 0) ? BN / 2 : BN;
+  constexpr int kOutCols = (kMode == 1) ? BN : BN / 2;
   constexpr int kStoresPerTile = EpiloguePlan<kMode>::kStores;
   static_assert(kLoadsPerStage + kStoresPerTile < 64, "vmcnt field is 6 bits");
   const int col_tiles = (Ncols + kOutCols - 1) / kOutCols;
@@ -194,7 +198,7 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     int ncol;
-    if (kMode == 0) ncol = (j < 2 ? 0 : BN / 2) + wn * 64 + (j % 2) * 32;
+    if (kMode != 1) ncol = (j < 2 ? 0 : BN / 2) + wn * 64 + (j % 2) * 32;
     else ncol = wn * 128 + j * 32;
     const int n = ncol + 16 * (g16 % 2) + 4 * (i16 % 4);
 #pragma unroll
@@ -258,7 +262,7 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
       const int c = (slot & 31) ^ (4 * (k & 3));
       const uint16_t* base;
       int col;
-      if (kMode == 0) {
+      if (kMode != 1) {
         base = (c < 16) ? B0 : B1;
         col = t.n0 + (c % 16) * 8;
       } else {
@@ -398,21 +402,37 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
     for (int i = 0; i < 2; ++i) {
       const int row = ci.row0 + wm * 64 + i * 32 + lane % 32;
       const bool row_ok = row < ci.row_end;
-      uint16_t* crow = C + int64_t(row_ok ? row : 0) * Ncols;
-      constexpr int kOutFrags = (kMode == 0) ? 2 : 4;
+      constexpr int kOutFrags = EpiloguePlan<kMode>::kOutFrags;
+      constexpr int64_t ldc = (kMode == 2) ? 2 : 1;
+      uint16_t* crow = C + int64_t(row_ok ? row : 0) * Ncols * ldc;
 #pragma unroll
       for (int jj = 0; jj < kOutFrags; ++jj) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const int col = ci.n0 + ((kMode == 0) ? wn * 64 : wn * 128) + jj * 32 + 8 * q +
+          const int col = ci.n0 + ((kMode == 1) ? wn * 128 : wn * 64) + jj * 32 + 8 * q +
                           4 * (lane / 32);
-          float v[4];
+          const bool ok = row_ok && col < Ncols;
+          float v[4], w[4];
+          float d[4] = {0.f, 0.f, 0.f, 0.f};
+          if (kMode == 2 && ok) {
+            const uint2 dh = *reinterpret_cast<const uint2*>(aux + int64_t(row) * Ncols + col);
+            d[0] = bf16_lo(dh.x);
+            d[1] = bf16_hi(dh.x);
+            d[2] = bf16_lo(dh.y);
+            d[3] = bf16_hi(dh.y);
+          }
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
             if (kMode == 0) {
               const float g = acc[i][jj][4 * q + k];
               const float u = acc[i][jj + 2][4 * q + k];
               v[k] = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+            } else if (kMode == 2) {
+              const float g = acc[i][jj][4 * q + k];
+              const float u = acc[i][jj + 2][4 * q + k];
+              const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+              v[k] = d[k] * u * sg * (1.0f + g * (1.0f - sg));  // dg
+              w[k] = d[k] * g * sg;                              // du
             } else {
               v[k] = acc[i][jj][4 * q + k];
             }
@@ -420,9 +440,15 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
           uint2 packed;
           packed.x = pack_bf16x2(v[0], v[1]);
           packed.y = pack_bf16x2(v[2], v[3]);
-          uint2* dst = (row_ok && col < Ncols) ? reinterpret_cast<uint2*>(crow + col)
-                                               : trash + lane;
+          uint2* dst = ok ? reinterpret_cast<uint2*>(crow + col) : trash + lane;
           *dst = packed;
+          if (kMode == 2) {
+            uint2 pw;
+            pw.x = pack_bf16x2(w[0], w[1]);
+            pw.y = pack_bf16x2(w[2], w[3]);
+            uint2* dw = ok ? reinterpret_cast<uint2*>(crow + Ncols + col) : trash + lane;
+            *dw = pw;
+          }
         }
       }
     }
@@ -458,10 +484,74 @@ hipError_t launch_grouped_gemm_swiglu(const uint16_t* x, const int32_t* offsets,
   if (N_cap == 0) return hipGetLastError();
   const int G = persistent_grid();
   uint2* trash = reinterpret_cast<uint2*>(static_cast<char*>(ws) + trash_offset(E));
-  hipLaunchKernelGGL(k_gemm<0>, dim3(G), dim3(kThreads), 0, st, x, H, wg, wu, I, w, E, h, trash);
+  hipLaunchKernelGGL(k_gemm<0>, dim3(G), dim3(kThreads), 0, st, x, H, wg, wu, I, w, E, h, trash,
+                     nullptr);
   hipLaunchKernelGGL(k_gemm<1>, dim3(G), dim3(kThreads), 0, st, h, I, wd, nullptr, H, w, E, y,
-                     trash);
+                     trash, nullptr);
   return hipGetLastError();
+}
+
+// Backward: dh = dy Wd^T (row-grouped), [dg | du] from the recomputed gate/up
+// tiles (mode 2), dx = [dg | du] [Wg ; Wu]^T (row-grouped), dWd = h^T dy and
+// [dWg | dWu] = x^T [dg | du] (sums over each expert's rows).
+// ws layout: forward tables (trash included) | backward tables | zeros[256 B]
+//            | dh [N_cap, I] bf16 | dgu [N_cap, 2I] bf16
+size_t gemm_grad_layout(int E, int64_t N_cap, int I, size_t* off_bt, size_t* off_zero,
+                        size_t* off_dh, size_t* off_dgu) {
+  const size_t fwd = ((gemm_workspace_bytes(E, N_cap, 0, 0) + 255) / 256) * 256;
+  *off_bt = fwd;
+  *off_zero = fwd + bgemm_sched_bytes(E);
+  *off_dh = *off_zero + 256;
+  *off_dgu = *off_dh + ((static_cast<size_t>(N_cap) * I * 2 + 255) / 256) * 256;
+  return *off_dgu + static_cast<size_t>(N_cap) * 2 * I * 2;
+}
+
+size_t gemm_grad_workspace_bytes(int E, int64_t N_cap, int /*H*/, int I) {
+  size_t a, b, c, d;
+  return gemm_grad_layout(E, N_cap, I, &a, &b, &c, &d);
+}
+
+namespace {
+__global__ void k_fill_zero(uint32_t* p, int n) {
+  if (static_cast<int>(threadIdx.x) < n) p[threadIdx.x] = 0u;
+}
+}  // namespace
+
+hipError_t launch_grouped_gemm_swiglu_grad(const uint16_t* x, const int32_t* offsets, int E,
+                                           int64_t N_cap, int H, int I, const uint16_t* wg,
+                                           const uint16_t* wu, const uint16_t* wd,
+                                           const uint16_t* h, const uint16_t* dy, uint16_t* dx,
+                                           uint16_t* dwg, uint16_t* dwu, uint16_t* dwd, void* ws,
+                                           hipStream_t st) {
+  size_t off_bt, off_zero, off_dh, off_dgu;
+  gemm_grad_layout(E, N_cap, I, &off_bt, &off_zero, &off_dh, &off_dgu);
+  char* base = static_cast<char*>(ws);
+  int32_t* w = static_cast<int32_t*>(ws);
+  int32_t* bt = reinterpret_cast<int32_t*>(base + off_bt);
+  uint16_t* zeros = reinterpret_cast<uint16_t*>(base + off_zero);
+  uint16_t* dh = reinterpret_cast<uint16_t*>(base + off_dh);
+  uint16_t* dgu = reinterpret_cast<uint16_t*>(base + off_dgu);
+  uint2* trash = reinterpret_cast<uint2*>(base + trash_offset(E));
+  hipLaunchKernelGGL(k_fill_zero, dim3(1), dim3(64), 0, st, reinterpret_cast<uint32_t*>(zeros), 64);
+  hipLaunchKernelGGL(k_gemm_sched, dim3(1), dim3(kSchedThreads), 0, st, offsets, E, N_cap, w);
+  hipError_t err = launch_bgemm_sched(offsets, E, N_cap, bt, st);
+  if (err != hipSuccess) return err;
+  if (N_cap > 0) {
+    // dh = dy Wd^T: B_e = Wd[e] as [I][H]
+    err = launch_bgemm_rows(dy, H, wd, wd, H, H, int64_t(I) * H, I, N_cap, bt, E, dh, st);
+    if (err != hipSuccess) return err;
+    // [dg | du] from the recomputed gate and up tiles
+    const int G = persistent_grid();
+    hipLaunchKernelGGL(k_gemm<2>, dim3(G), dim3(kThreads), 0, st, x, H, wg, wu, I, w, E, dgu,
+                       trash, dh);
+    // dx = [dg | du] [Wg ; Wu]^T: B_e = Wg[e], Wu[e] as [H][I] side by side along k
+    err = launch_bgemm_rows(dgu, 2 * I, wg, wu, I, I, int64_t(H) * I, H, N_cap, bt, E, dx, st);
+    if (err != hipSuccess) return err;
+  }
+  // dWd = h^T dy  ([E, I, H]),  [dWg | dWu] = x^T [dg | du]  ([E, H, I] each)
+  err = launch_bgemm_kgroup(h, I, I, dy, H, H, bt, E, zeros, dwd, dwd, H, H, st);
+  if (err != hipSuccess) return err;
+  return launch_bgemm_kgroup(x, H, H, dgu, 2 * I, 2 * I, bt, E, zeros, dwg, dwu, I, I, st);
 }
 
 }  // namespace moe

@@ -1,0 +1,374 @@
+// Grouped GEMMs of the SwiGLU expert FFN backward (gfx950 bf16 MFMA).
+//
+// Follows the twinkle grouped-matmul PR ("feat(moe): NPU平台 EP experts forward
+// 计算改用 NPU grouped matmul"), differentiated: with dh = dy Wd^T and
+// (dg, du) from the SwiGLU derivative,
+//   dx  = [dg | du] [Wg ; Wu]^T        (rows grouped by expert, like the forward)
+//   dWd = h^T dy,  [dWg | dWu] = x^T [dg | du]   (sums over each expert's rows)
+//
+// Two tile kernels share one 128 x 128 x 64 tile (256 threads as 2 x 2 waves,
+// each 64 x 64 = 2 x 2 accumulators of v_mfma_f32_32x32x16_bf16, fp32):
+//  - k_bgemm_rows: C[rows of e, :] = A[rows of e, :] B_e^T with A [row][k] and
+//    B_e [n][k] (both k-contiguous). B may be two matrices side by side along k
+//    (Wg then Wu).
+//  - k_bgemm_kgroup: C_e = A_e^T B_e with A_e [rows of e][m] and B_e [rows of
+//    e][n] (both row-contiguous): the contraction runs over the expert's rows,
+//    its ragged tail is zero-filled, and an expert without rows gets a zero
+//    tile. Tiles go out biggest expert first.
+// Operands are staged global -> registers -> LDS, double-buffered (the next
+// k-step's loads are in flight during this one's MFMAs). k-contiguous tiles sit
+// in LDS as [row][k] with the XOR swizzle of the forward kernel and are read
+// with ds_read_b128; row-contiguous tiles sit as [k][col] and the MFMA operand
+// (8 consecutive k of one column per lane) is formed by ds_read_b64_tr_b16
+// transpose reads, as the forward kernel does for its weights.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
+
+constexpr int TM = 128, TN = 128, TK = 64;
+constexpr int kThreads = 256;
+constexpr int kTileChunks = TM * TK / 8;             // 16-byte chunks per operand tile
+constexpr int kLoads = kTileChunks / kThreads;        // per thread per operand per step
+constexpr int kTileBytes = kTileChunks * 16;
+constexpr int kStageBytes = 2 * kTileBytes;
+constexpr int kSchedThreads = 1024;
+
+// [row][k] tile: row r, 16-byte k-chunk kc (8 per row)
+__device__ __forceinline__ int swz_rk(int r, int kc) { return r * (TK / 8) + (kc ^ ((r >> 1) & 7)); }
+// [k][col] tile: k row, 16-byte column chunk c (16 per row)
+__device__ __forceinline__ int swz_kc(int k, int c) { return k * (TM / 8) + (c ^ (4 * (k & 3))); }
+
+// MFMA operand (rows base + lane % 32, k = 16 kk + 8 (lane / 32) + 0..7) of a [row][k] tile
+__device__ __forceinline__ bf16x8_t read_rk(const lds_u8_t* t, int base, int kk, int lane) {
+  const int slot = swz_rk(base + lane % 32, kk * 2 + lane / 32);
+  const u32x4_t v = *(const __attribute__((address_space(3))) u32x4_t*)(t + slot * 16);
+  bf16x8_t r;
+  __builtin_memcpy(&r, &v, 16);
+  return r;
+}
+
+// Byte offsets of the two transpose reads that form the operand of columns
+// col0 .. col0 + 31 of a [k][col] tile at k-substep 0 (substep kk adds 16 k
+// rows, which keeps k & 3 and so the swizzle): within each group of 16 lanes,
+// input lane i points at k row i / 4 (+ 4 for the second read), column 4 (i % 4).
+__device__ __forceinline__ void tr_offsets(int col0, int lane, int off[2]) {
+  const int g16 = lane / 16, i16 = lane % 16;
+  const int n = col0 + 16 * (g16 % 2) + 4 * (i16 % 4);
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int k = 8 * (g16 / 2) + i16 / 4 + 4 * half;
+    off[half] = swz_kc(k, n / 8) * 16 + (n % 8) * 2;
+  }
+}
+
+__device__ __forceinline__ bf16x8_t read_kc(const lds_u8_t* t, const int off[2], int kk) {
+  const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(t + off[0] + kk * 16 * (TM * 2)));
+  const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(t + off[1] + kk * 16 * (TM * 2)));
+  bf16x8_t r;
+  __builtin_memcpy(&r, &lo, 8);
+  __builtin_memcpy(reinterpret_cast<char*>(&r) + 8, &hi, 8);
+  return r;
+}
+
+__device__ __forceinline__ void st_lds16(lds_u8_t* t, int slot, const uint4& v) {
+  const u32x4_t u = {v.x, v.y, v.z, v.w};
+  *(__attribute__((address_space(3))) u32x4_t*)(t + slot * 16) = u;
+}
+
+// Stores of one wave's 64 x 64 accumulator block: row m = m0 + 32 i + lane % 32,
+// four consecutive columns n = n0 + 32 j + 8 q + 4 (lane / 32) per 8-byte store.
+// Columns at or past `split` go to C1 at column n - split.
+__device__ __forceinline__ void store_block(const f32x16_t acc[2][2], int m0, int m_end, int n0,
+                                            int n_end, int split, uint16_t* C0, uint16_t* C1,
+                                            int64_t ldc, int lane) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int m = m0 + 32 * i + lane % 32;
+    if (m >= m_end) continue;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + 32 * j + 8 * q + 4 * (lane / 32);
+        if (n >= n_end) continue;
+        uint2 packed;
+        packed.x = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
+        packed.y = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
+        uint16_t* dst = n < split ? C0 + int64_t(m) * ldc + n : C1 + int64_t(m) * ldc + (n - split);
+        *reinterpret_cast<uint2*>(dst) = packed;
+      }
+  }
+}
+
+// ws layout (int32): prefix[E+1] | offs[E+1] | order[E]
+//   prefix: row-tile prefix (ceil(rows_e / TM) per expert), offs: clamped
+//   offsets, order: experts by row count, largest first (ties: lower id first).
+__global__ void __launch_bounds__(kSchedThreads)
+k_bgemm_sched(const int32_t* __restrict__ offsets, int E, int64_t N_cap, int32_t* __restrict__ ws) {
+  __shared__ int32_t part[kSchedThreads];
+  __shared__ int32_t rows[kSchedThreads];
+  int32_t* prefix = ws;
+  int32_t* offs = ws + (E + 1);
+  int32_t* order = ws + 2 * (E + 1);
+  const int e = threadIdx.x;
+  int32_t lo = 0, hi = 0;
+  if (e < E) {
+    lo = static_cast<int32_t>(std::min<int64_t>(std::max(offsets[e], 0), N_cap));
+    hi = static_cast<int32_t>(std::min<int64_t>(std::max(offsets[e + 1], 0), N_cap));
+    hi = std::max(hi, lo);
+  }
+  rows[e] = hi - lo;
+  const int32_t tiles = (e < E) ? (hi - lo + TM - 1) / TM : 0;
+  part[e] = tiles;
+  __syncthreads();
+  for (int off = 1; off < kSchedThreads; off <<= 1) {
+    const int32_t v = e >= off ? part[e - off] : 0;
+    __syncthreads();
+    part[e] += v;
+    __syncthreads();
+  }
+  if (e < E) {
+    prefix[e] = part[e] - tiles;
+    offs[e] = lo;
+    if (e == E - 1) {
+      prefix[E] = part[e];
+      offs[E] = hi;
+    }
+    int rank = 0;
+    const int32_t mine = rows[e];
+    for (int o = 0; o < E; ++o) rank += (rows[o] > mine || (rows[o] == mine && o < e)) ? 1 : 0;
+    order[rank] = e;
+  }
+}
+
+// Row-grouped C = A B^T. A [rows][K] (lda = K), B_e = B0/B1 + e * strideB with
+// element (n, k) at n * ldb + k for k < ksplit (B0) and n * ldb + k - ksplit
+// (B1) otherwise. Grid: an upper bound of the row tiles times the column tiles.
+__global__ void __launch_bounds__(kThreads, 2)
+k_bgemm_rows(const uint16_t* __restrict__ A, int K, const uint16_t* __restrict__ B0,
+             const uint16_t* __restrict__ B1, int ksplit, int64_t ldb, int64_t strideB, int Ncols,
+             const int32_t* __restrict__ ws, int E, uint16_t* __restrict__ C) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStageBytes];
+  lds_u8_t* lds = (lds_u8_t*)smem;
+  const int32_t* prefix = ws;
+  const int32_t* offs = ws + (E + 1);
+  const int col_tiles = (Ncols + TN - 1) / TN;
+  const int rt = static_cast<int>(blockIdx.x) / col_tiles;
+  const int ct = static_cast<int>(blockIdx.x) % col_tiles;
+  if (rt >= prefix[E]) return;
+  int lo = 0, hi = E;  // expert of row tile rt: last e with prefix[e] <= rt
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (prefix[mid] <= rt) lo = mid; else hi = mid;
+  }
+  const int e = lo;
+  const int row0 = offs[e] + (rt - prefix[e]) * TM;
+  const int row_end = std::min(row0 + TM, offs[e + 1]);
+  const int n0 = ct * TN;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int wm = wave & 1, wn = wave >> 1;
+
+  // this thread's chunks: tile row c / 8, k-chunk c % 8 (8 threads per 128-byte row)
+  const uint16_t* a_src[kLoads];
+  int64_t b_row[kLoads];
+  int slot[kLoads];
+#pragma unroll
+  for (int l = 0; l < kLoads; ++l) {
+    const int c = l * kThreads + tid;
+    const int r = c >> 3, kc = c & 7;
+    slot[l] = swz_rk(r, kc);
+    a_src[l] = A + int64_t(std::min(row0 + r, row_end - 1)) * K + kc * 8;
+    b_row[l] = int64_t(e) * strideB + int64_t(std::min(n0 + r, Ncols - 1)) * ldb + kc * 8;
+  }
+  uint4 ra[kLoads], rb[kLoads];
+  auto load = [&](int ks) {
+    const int k0 = ks * TK;
+    const uint16_t* bb = k0 < ksplit ? B0 : B1;
+    const int kb = k0 < ksplit ? k0 : k0 - ksplit;
+#pragma unroll
+    for (int l = 0; l < kLoads; ++l) {
+      ra[l] = *reinterpret_cast<const uint4*>(a_src[l] + k0);
+      rb[l] = *reinterpret_cast<const uint4*>(bb + b_row[l] + kb);
+    }
+  };
+  auto stash = [&](int buf) {
+    lds_u8_t* st = lds + buf * kStageBytes;
+#pragma unroll
+    for (int l = 0; l < kLoads; ++l) {
+      st_lds16(st, slot[l], ra[l]);
+      st_lds16(st + kTileBytes, slot[l], rb[l]);
+    }
+  };
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  const int ksteps = K / TK;
+  load(0);
+  stash(0);
+  __syncthreads();
+  for (int ks = 0; ks < ksteps; ++ks) {
+    const int buf = ks & 1;
+    if (ks + 1 < ksteps) load(ks + 1);
+    const lds_u8_t* ta = lds + buf * kStageBytes;
+    const lds_u8_t* tb = ta + kTileBytes;
+#pragma unroll
+    for (int kk = 0; kk < TK / 16; ++kk) {
+      bf16x8_t fa[2], fb[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) fa[i] = read_rk(ta, wm * 64 + 32 * i, kk, lane);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) fb[j] = read_rk(tb, wn * 64 + 32 * j, kk, lane);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+    }
+    if (ks + 1 < ksteps) stash(buf ^ 1);
+    __syncthreads();
+  }
+  store_block(acc, row0 + wm * 64, row_end, n0 + wn * 64, Ncols, Ncols, C, C, Ncols, lane);
+}
+
+// k-grouped C_e = A_e^T B_e over the rows of expert e: A rows [row][m] (lda),
+// B rows [row][n] (ldb); C_e is [M][N] at C0 + e * M * ldc (columns at or past
+// `split` go to C1 + e * M * ldc at column n - split). Grid: E * m-tiles *
+// n-tiles, experts taken in `order` (largest first).
+__global__ void __launch_bounds__(kThreads, 2)
+k_bgemm_kgroup(const uint16_t* __restrict__ A, int64_t lda, int M, const uint16_t* __restrict__ B,
+               int64_t ldb, int N, const int32_t* __restrict__ ws, int E,
+               const uint16_t* __restrict__ zeros, uint16_t* __restrict__ C0,
+               uint16_t* __restrict__ C1, int split, int64_t ldc) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStageBytes];
+  lds_u8_t* lds = (lds_u8_t*)smem;
+  const int32_t* offs = ws + (E + 1);
+  const int32_t* order = ws + 2 * (E + 1);
+  const int mt_n = (M + TM - 1) / TM, nt_n = (N + TN - 1) / TN;
+  const int per_e = mt_n * nt_n;
+  const int e = order[static_cast<int>(blockIdx.x) / per_e];
+  const int t = static_cast<int>(blockIdx.x) % per_e;
+  const int m0 = (t / nt_n) * TM, n0 = (t % nt_n) * TN;
+  const int r_lo = offs[e], r_hi = offs[e + 1];
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int wm = wave & 1, wn = wave >> 1;
+
+  // this thread's chunks: k row c / 16, column chunk c % 16 (16 threads per 256-byte row)
+  int slot[kLoads], krow[kLoads], colA[kLoads], colB[kLoads];
+#pragma unroll
+  for (int l = 0; l < kLoads; ++l) {
+    const int c = l * kThreads + tid;
+    krow[l] = c >> 4;
+    const int cc = c & 15;
+    slot[l] = swz_kc(krow[l], cc);
+    colA[l] = std::min(m0 + cc * 8, M - 8);
+    colB[l] = std::min(n0 + cc * 8, N - 8);
+  }
+  uint4 ra[kLoads], rb[kLoads];
+  auto load = [&](int r0) {
+#pragma unroll
+    for (int l = 0; l < kLoads; ++l) {
+      const int r = r0 + krow[l];
+      const bool in = r < r_hi;  // the ragged tail reads zeros
+      const uint16_t* pa = in ? A + int64_t(r) * lda + colA[l] : zeros;
+      const uint16_t* pb = in ? B + int64_t(r) * ldb + colB[l] : zeros;
+      ra[l] = *reinterpret_cast<const uint4*>(pa);
+      rb[l] = *reinterpret_cast<const uint4*>(pb);
+    }
+  };
+  auto stash = [&](int buf) {
+    lds_u8_t* st = lds + buf * kStageBytes;
+#pragma unroll
+    for (int l = 0; l < kLoads; ++l) {
+      st_lds16(st, slot[l], ra[l]);
+      st_lds16(st + kTileBytes, slot[l], rb[l]);
+    }
+  };
+  int offA[2][2], offB[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) tr_offsets(wm * 64 + 32 * i, lane, offA[i]);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) tr_offsets(wn * 64 + 32 * j, lane, offB[j]);
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  const int ksteps = static_cast<int>(ceil_div(r_hi - r_lo, TK));
+  if (ksteps > 0) {
+    load(r_lo);
+    stash(0);
+    __syncthreads();
+  }
+  for (int ks = 0; ks < ksteps; ++ks) {
+    const int buf = ks & 1;
+    if (ks + 1 < ksteps) load(r_lo + (ks + 1) * TK);
+    const lds_u8_t* ta = lds + buf * kStageBytes;
+    const lds_u8_t* tb = ta + kTileBytes;
+#pragma unroll
+    for (int kk = 0; kk < TK / 16; ++kk) {
+      bf16x8_t fa[2], fb[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) fa[i] = read_kc(ta, offA[i], kk);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) fb[j] = read_kc(tb, offB[j], kk);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
+    }
+    if (ks + 1 < ksteps) stash(buf ^ 1);
+    __syncthreads();
+  }
+  const int64_t ebase = int64_t(e) * M * ldc;
+  store_block(acc, m0 + wm * 64, M, n0 + wn * 64, N, split, C0 + ebase, C1 + ebase, ldc, lane);
+}
+
+}  // namespace
+
+size_t bgemm_sched_bytes(int E) {
+  return ((static_cast<size_t>(3 * E + 2) * 4 + 255) / 256) * 256;
+}
+
+hipError_t launch_bgemm_sched(const int32_t* offsets, int E, int64_t N_cap, int32_t* ws,
+                              hipStream_t st) {
+  hipLaunchKernelGGL(k_bgemm_sched, dim3(1), dim3(kSchedThreads), 0, st, offsets, E, N_cap, ws);
+  return hipGetLastError();
+}
+
+hipError_t launch_bgemm_rows(const uint16_t* A, int K, const uint16_t* B0, const uint16_t* B1,
+                             int ksplit, int64_t ldb, int64_t strideB, int Ncols, int64_t N_cap,
+                             const int32_t* ws, int E, uint16_t* C, hipStream_t st) {
+  if (N_cap == 0) return hipGetLastError();
+  const int64_t row_tiles = ceil_div(N_cap, TM) + E;  // at least the real row tiles
+  const int64_t grid = row_tiles * ceil_div(Ncols, TN);
+  hipLaunchKernelGGL(k_bgemm_rows, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, st, A, K,
+                     B0, B1, ksplit, ldb, strideB, Ncols, ws, E, C);
+  return hipGetLastError();
+}
+
+hipError_t launch_bgemm_kgroup(const uint16_t* A, int64_t lda, int M, const uint16_t* B,
+                               int64_t ldb, int N, const int32_t* ws, int E,
+                               const uint16_t* zeros, uint16_t* C0, uint16_t* C1, int split,
+                               int64_t ldc, hipStream_t st) {
+  const int64_t grid = int64_t(E) * ceil_div(M, TM) * ceil_div(N, TN);
+  hipLaunchKernelGGL(k_bgemm_kgroup, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, st, A,
+                     lda, M, B, ldb, N, ws, E, zeros, C0, C1, split, ldc);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -484,24 +484,31 @@ def main():
                 "avg_us": round(g_us, 2), "flops_per_launch": gemm_flops(n_rows, H, I),
                 "algorithmic_bytes_per_launch": gemm_bytes(n_rows, H, I, active),
                 "hbm_gbs_algorithmic": round(gemm_bytes(n_rows, H, I, active) / (g_us * 1e-6) / 1e9, 1)}
-    layer_ops = [
-        dict(workload=c["name"], **op_entry("permute", float(np.median(seg[:, 0])),
-                                            float(np.min(seg[:, 0])),
-                                            nbytes=permute_bytes(T, K, H, n_rows))),
-        dict(workload=c["name"], **op_entry("grouped_gemm_swiglu", float(np.median(seg[:, 1])),
-                                            float(np.min(seg[:, 1])),
-                                            flops=gemm_flops(n_rows, H, I))),
-        dict(workload=c["name"], **op_entry("unpermute_combine", float(np.median(seg[:, 2])),
-                                            float(np.min(seg[:, 2])),
-                                            nbytes=combine_bytes(T, K, H, n_rows))),
-        dict(workload=c["name"], **op_entry("unpermute_grad", float(np.median(seg[:, 3])),
-                                            float(np.min(seg[:, 3])),
-                                            nbytes=grad_bytes(T, K, H, n_rows))),
-    ]
+    # per-op figures of the layer's memory-bound calls: each call timed alone with
+    # a 1 GiB write between launches (nothing left in the 256 MB Infinity Cache);
+    # with --no-ops, the in-step times instead (marked as such)
+    permute, _, combine, grad = step_calls(d)
+    flush = None if args.no_ops else Flusher(dev)
+    mem_ops = (("permute", permute, 0, permute_bytes(T, K, H, n_rows)),
+               ("unpermute_combine", combine, 2, combine_bytes(T, K, H, n_rows)),
+               ("unpermute_grad", grad, 3, grad_bytes(T, K, H, n_rows)))
+    layer_ops = []
+    for name, fn, col, nbytes in mem_ops:
+        if flush is not None:
+            us, usmin = time_op(fn, args.op_iters, flush)
+            timing = "alone, cache flushed"
+        else:
+            us, usmin = float(np.median(seg[:, col])), float(np.min(seg[:, col]))
+            timing = "in the layer step"
+        layer_ops.append(dict(workload=c["name"], timing=timing,
+                              **op_entry(name, us, usmin, nbytes=nbytes)))
+    layer_ops.insert(1, dict(workload=c["name"], timing="in the layer step",
+                             **op_entry("grouped_gemm_swiglu", float(np.median(seg[:, 1])),
+                                        float(np.min(seg[:, 1])),
+                                        flops=gemm_flops(n_rows, H, I))))
     ops = layer_ops
     if not args.no_ops:
         ops.append(dict(workload=c["name"], **gemm_grad_op(args, d, n_rows)))
-        flush = Flusher(dev)
         ops = ops + run_ops(args, dev, flush)
         del flush
     cpu = None

@@ -32,8 +32,13 @@ __global__ void __launch_bounds__(kWaves * kWave)
 k_combine(const uint16_t* __restrict__ expert_out, int64_t N, const int32_t* __restrict__ row_of_slot,
           const int32_t* __restrict__ row_map, const int32_t* __restrict__ ids,
           const float* __restrict__ probs, SlotMask mk, int64_t T, int K, int H, int E,
-          SpecialArgs sp, const uint16_t* __restrict__ shared_x, uint16_t* __restrict__ out) {
-  const int64_t t = uniform(static_cast<int>(blockIdx.x * kWaves + threadIdx.x / kWave));
+          SpecialArgs sp, const uint16_t* __restrict__ shared_x, uint16_t* __restrict__ out,
+          int nsplit) {
+  // nsplit waves share a token, each taking every nsplit-th 64-chunk row of
+  // the hidden dim (each writes its own part of the output row)
+  const int w = threadIdx.x / kWave;
+  const int part = w % nsplit;
+  const int64_t t = uniform(static_cast<int>(blockIdx.x * (kWaves / nsplit) + w / nsplit));
   if (t >= T) return;
   const int lane = threadIdx.x % kWave;
   const int64_t copy_lo = int64_t(E) + sp.num_zero;
@@ -90,7 +95,7 @@ k_combine(const uint16_t* __restrict__ expert_out, int64_t N, const int32_t* __r
 
   const int chunks = H / 8;
   const uint16_t* orow = need_ori ? sp.ori_x + t * H : nullptr;
-  for (int c = lane; c < chunks; c += kWave) {
+  for (int c = lane + part * kWave; c < chunks; c += kWave * nsplit) {
     const int h0 = c * 8;
     float acc[8];
 #pragma unroll
@@ -142,6 +147,10 @@ k_combine(const uint16_t* __restrict__ expert_out, int64_t N, const int32_t* __r
   }
 }
 
+// Two waves per token when there are too few tokens to give every SIMD
+// several rounds of waves and each row has at least two 64-chunk rows.
+int split_for(int64_t T, int H) { return (H / 8 >= 2 * kWave && T < kSplitBelowTokens) ? 2 : 1; }
+
 }  // namespace
 
 hipError_t launch_combine(const uint16_t* expert_out, int64_t N, const int32_t* row_of_slot,
@@ -149,12 +158,13 @@ hipError_t launch_combine(const uint16_t* expert_out, int64_t N, const int32_t* 
                           SlotMask mk, int64_t T, int K, int H, int E, const SpecialArgs& sp,
                           const uint16_t* shared_x, uint16_t* out, hipStream_t st) {
   if (T == 0) return hipGetLastError();
-  const dim3 grid(static_cast<unsigned>(ceil_div(T, kWaves)));
+  const int nsplit = split_for(T, H);
+  const dim3 grid(static_cast<unsigned>(ceil_div(T, kWaves / nsplit)));
   const dim3 block(kWaves * kWave);
   const bool per_h = sp.num_const > 0 && sp.a_sh != 0;
 #define MOE_COMBINE(RM, PH)                                                                    \
   hipLaunchKernelGGL((k_combine<RM, PH>), grid, block, 0, st, expert_out, N, row_of_slot,     \
-                     row_map, ids, probs, mk, T, K, H, E, sp, shared_x, out)
+                     row_map, ids, probs, mk, T, K, H, E, sp, shared_x, out, nsplit)
   if (row_map != nullptr) {
     if (per_h) MOE_COMBINE(true, true); else MOE_COMBINE(true, false);
   } else {
@@ -167,11 +177,12 @@ hipError_t launch_combine(const uint16_t* expert_out, int64_t N, const int32_t* 
 hipError_t launch_permute_grad(const uint16_t* d_permuted, int64_t N, const int32_t* row_of_slot,
                                int64_t T, int K, int H, uint16_t* d_x, hipStream_t st) {
   if (T == 0) return hipGetLastError();
-  const dim3 grid(static_cast<unsigned>(ceil_div(T, kWaves)));
+  const int nsplit = split_for(T, H);
+  const dim3 grid(static_cast<unsigned>(ceil_div(T, kWaves / nsplit)));
   const dim3 block(kWaves * kWave);
   hipLaunchKernelGGL((k_combine<false, false, true>), grid, block, 0, st, d_permuted, N,
                      row_of_slot, nullptr, nullptr, nullptr, SlotMask{nullptr, 0, K}, T, K, H, 0,
-                     SpecialArgs{}, nullptr, d_x);
+                     SpecialArgs{}, nullptr, d_x, nsplit);
   return hipGetLastError();
 }
 

@@ -548,7 +548,7 @@ hipError_t launch_combine_grad(const uint16_t* grad_out, const uint16_t* expert_
   {
     // two waves per token once a token's row is long and there are too few
     // tokens to keep every SIMD busy for several rounds
-    const int nsplit = (H / 8 >= 2 * kWave && T < 32768) ? 2 : 1;
+    const int nsplit = (H / 8 >= 2 * kWave && T < 2 * kSplitBelowTokens) ? 2 : 1;
     const dim3 grid(static_cast<unsigned>(ceil_div(T, kWaves / nsplit)));
     const dim3 block(kWaves * kWave);
 #define MOE_CGRAD(RM, PH, MK)                                                                  \

@@ -10,6 +10,11 @@ namespace moe {
 
 constexpr int kWave = 64;
 
+// Below this many tokens the row kernels (permute rows, combine) give each
+// token two waves, each taking every other 64-chunk row of the hidden dim: a
+// wave per token would leave too few waves for several rounds on 1024 SIMDs.
+constexpr int64_t kSplitBelowTokens = 16384;
+
 // 16-byte vector of 8 bf16 values, moved as four dwords.
 struct alignas(16) Vec8 {
   uint32_t w[4];

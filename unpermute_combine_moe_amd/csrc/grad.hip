@@ -6,10 +6,13 @@
 // permuted_tokens, which stays sharded on the hidden dim (elementwise in h),
 // and the gradient of probs, which is Partial() (a sum over h).
 //
-// One wave per token. The token's grad_out row is loaded once into registers
-// (kCpl 16-byte chunks per lane); for each slot the wave streams the permuted
-// row in, writes p * g as correctly rounded bf16, and reduces the fp32 dot
-// product across the wave.
+// One wave per token. The slots' rows and probabilities are read once (lane k
+// for slot k, broadcast by readlane) and the token's grad_out row is kept in
+// registers (kCpl 16-byte chunks per lane, packed bf16); the wave then streams
+// the permuted rows slot by slot, writes p * g as correctly rounded bf16 and
+// reduces each slot's fp32 dot product. (Loading slot k + 1's row during slot
+// k was measured slower: the extra registers cost more occupancy than the
+// overlap gains.)
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -28,51 +31,64 @@ k_unpermute_grad(const uint16_t* __restrict__ grad_out, const uint16_t* __restri
   if (t >= T) return;
   const int lane = threadIdx.x % kWave;
   const int chunks = H / 8;
-  float g[kCpl][8];
+  // slot metadata up front: lane k loads slot k, readlane broadcasts it
+  int m_row = -1;
+  float m_p = 0.f;
+  if (lane < K) {
+    const int64_t r = row_of_slot[t * K + lane];
+    m_row = (r >= 0 && r < N) ? static_cast<int>(r) : -1;
+    m_p = probs[t * K + lane];
+  }
+  int row[16];
+  float p[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    row[k] = k < K ? __builtin_amdgcn_readlane(m_row, k) : -1;
+    p[k] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m_p), k));
+  }
+  // the token's grad_out row stays packed (bf16) in registers
+  Vec8 g[kCpl];
 #pragma unroll
   for (int j = 0; j < kCpl; ++j) {
     const int c = lane + j * kWave;
-    if (c < chunks) unpack8(load16(grad_out + t * H + c * 8), g[j]);
-    else
-#pragma unroll
-      for (int i = 0; i < 8; ++i) g[j][i] = 0.f;
+    g[j] = c < chunks ? load16(grad_out + t * H + c * 8) : Vec8{{0u, 0u, 0u, 0u}};
   }
-  for (int k = 0; k < K; ++k) {
-    const int64_t s = t * K + k;
-    const int64_t row = row_of_slot[s];
-    if (row < 0 || row >= N) {
-      if (lane == 0) d_probs[s] = 0.f;
-      continue;
-    }
-    const float p = probs[s];
-    const uint16_t* prow = permuted + row * H;
-    uint16_t* drow = d_permuted + row * H;
-    Vec8 pv[kCpl];
+  float mine = 0.f;
 #pragma unroll
-    for (int j = 0; j < kCpl; ++j) {
-      const int c = lane + j * kWave;
-      if (c < chunks) pv[j] = load16_nt(prow + c * 8);
-    }
+  for (int k = 0; k < 16; ++k) {
+    if (k >= K) break;
     float dot = 0.f;
+    if (row[k] >= 0) {
+      Vec8 v[kCpl];
 #pragma unroll
-    for (int j = 0; j < kCpl; ++j) {
-      const int c = lane + j * kWave;
-      if (c < chunks) {
-        float f[8];
-        unpack8(pv[j], f);
-        Vec8 d;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          d.w[i] = mul_to_bf16_exact(p, g[j][2 * i]) | (mul_to_bf16_exact(p, g[j][2 * i + 1]) << 16);
-          dot = __builtin_fmaf(g[j][2 * i], f[2 * i], dot);
-          dot = __builtin_fmaf(g[j][2 * i + 1], f[2 * i + 1], dot);
-        }
-        store16(drow + c * 8, d);
+      for (int j = 0; j < kCpl; ++j) {
+        const int c = lane + j * kWave;
+        if (c < chunks) v[j] = load16_nt(permuted + int64_t(row[k]) * H + c * 8);
       }
+      uint16_t* drow = d_permuted + int64_t(row[k]) * H;
+#pragma unroll
+      for (int j = 0; j < kCpl; ++j) {
+        const int c = lane + j * kWave;
+        if (c < chunks) {
+          float f[8], gf[8];
+          unpack8(v[j], f);
+          unpack8(g[j], gf);
+          Vec8 d;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            d.w[i] = mul_to_bf16_exact(p[k], gf[2 * i]) |
+                     (mul_to_bf16_exact(p[k], gf[2 * i + 1]) << 16);
+            dot = __builtin_fmaf(gf[2 * i], f[2 * i], dot);
+            dot = __builtin_fmaf(gf[2 * i + 1], f[2 * i + 1], dot);
+          }
+          store16(drow + c * 8, d);
+        }
+      }
+      dot = wave_sum(dot);
     }
-    dot = wave_sum(dot);
-    if (lane == 0) d_probs[s] = dot;
+    if (lane == k) mine = dot;  // 0 for a slot without a row
   }
+  if (lane < K) d_probs[t * K + lane] = mine;
 }
 
 // Hidden sizes beyond kCpl = 16 (H > 8192): loop over chunks, re-reading the

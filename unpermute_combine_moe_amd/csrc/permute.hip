@@ -242,8 +242,11 @@ k_route_empty(int E, int32_t* __restrict__ counts, int32_t* __restrict__ offsets
 constexpr int kRowWaves = 4;
 __global__ void __launch_bounds__(kRowWaves * kWave)
 k_permute_rows(const uint16_t* __restrict__ x, const int32_t* __restrict__ row_of_slot,
-               int64_t T, int H, int K, int64_t S, uint16_t* __restrict__ permuted) {
-  const int64_t t = uniform(static_cast<int>(blockIdx.x * kRowWaves + threadIdx.x / kWave));
+               int64_t T, int H, int K, int64_t S, uint16_t* __restrict__ permuted, int nsplit) {
+  // nsplit waves share a token, each taking every nsplit-th 64-chunk row of it
+  const int w = threadIdx.x / kWave;
+  const int part = w % nsplit;
+  const int64_t t = uniform(static_cast<int>(blockIdx.x * (kRowWaves / nsplit) + w / nsplit));
   if (t >= T) return;
   const int lane = threadIdx.x % kWave;
   int32_t rows[16];
@@ -251,7 +254,7 @@ k_permute_rows(const uint16_t* __restrict__ x, const int32_t* __restrict__ row_o
   for (int k = 0; k < 16; ++k) rows[k] = (k < K) ? row_of_slot[t * K + k] : -1;
   const int chunks = H / 8;
   const uint16_t* src = x + t * H;
-  for (int c = lane; c < chunks; c += kWave) {
+  for (int c = lane + part * kWave; c < chunks; c += kWave * nsplit) {
     const Vec8 v = load16_nt(src + c * 8);
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
@@ -284,8 +287,12 @@ hipError_t launch_permute(const uint16_t* x, const int32_t* ids, SlotMask mk, in
                      dim3(kChunkThreads), lds, st, ids, mk, S, E, p.iters, p.nblk, table, counts,
                      offsets, sorted_slot, row_of_slot);
   if (permuted != nullptr) {
-    hipLaunchKernelGGL(k_permute_rows, dim3(static_cast<unsigned>(ceil_div(T, kRowWaves))),
-                       dim3(kRowWaves * kWave), 0, st, x, row_of_slot, T, H, K, S, permuted);
+    // two waves per token when there are too few tokens for several rounds of waves
+    const int nsplit = (H / 8 >= 2 * kWave && T < kSplitBelowTokens) ? 2 : 1;
+    hipLaunchKernelGGL(k_permute_rows,
+                       dim3(static_cast<unsigned>(ceil_div(T, kRowWaves / nsplit))),
+                       dim3(kRowWaves * kWave), 0, st, x, row_of_slot, T, H, K, S, permuted,
+                       nsplit);
   }
   return hipGetLastError();
 }

@@ -26,15 +26,23 @@ __global__ void __launch_bounds__(kWaves * kWave)
 k_unpermute_grad(const uint16_t* __restrict__ grad_out, const uint16_t* __restrict__ permuted,
                  int64_t N, const int32_t* __restrict__ row_of_slot,
                  const float* __restrict__ probs, int64_t T, int K, int H,
-                 uint16_t* __restrict__ d_permuted, float* __restrict__ d_probs) {
-  const int64_t t = uniform(static_cast<int>(blockIdx.x * kWaves + threadIdx.x / kWave));
-  if (t >= T) return;
+                 uint16_t* __restrict__ d_permuted, float* __restrict__ d_probs, int nsplit) {
+  // nsplit waves share a token: part q takes the 64-chunk rows q, q + nsplit, ...
+  // of the hidden dim, and the per-slot partial dot products meet in LDS
+  __shared__ float xch[kWaves][16];
+  const int w = threadIdx.x / kWave;
+  const int part = w % nsplit;
+  const int64_t t = uniform(static_cast<int>(blockIdx.x * (kWaves / nsplit) + w / nsplit));
+  const bool live = t < T;
+  if (nsplit == 1 && !live) return;
   const int lane = threadIdx.x % kWave;
-  const int chunks = H / 8;
+  const int chunks = live ? H / 8 : 0;
+  // this lane's chunk j of the row: 64-chunk row j * nsplit + part
+  auto chunk = [&](int j) { return lane + (j * nsplit + part) * kWave; };
   // slot metadata up front: lane k loads slot k, readlane broadcasts it
   int m_row = -1;
   float m_p = 0.f;
-  if (lane < K) {
+  if (live && lane < K) {
     const int64_t r = row_of_slot[t * K + lane];
     m_row = (r >= 0 && r < N) ? static_cast<int>(r) : -1;
     m_p = probs[t * K + lane];
@@ -50,7 +58,7 @@ k_unpermute_grad(const uint16_t* __restrict__ grad_out, const uint16_t* __restri
   Vec8 g[kCpl];
 #pragma unroll
   for (int j = 0; j < kCpl; ++j) {
-    const int c = lane + j * kWave;
+    const int c = chunk(j);
     g[j] = c < chunks ? load16(grad_out + t * H + c * 8) : Vec8{{0u, 0u, 0u, 0u}};
   }
   float mine = 0.f;
@@ -62,13 +70,13 @@ k_unpermute_grad(const uint16_t* __restrict__ grad_out, const uint16_t* __restri
       Vec8 v[kCpl];
 #pragma unroll
       for (int j = 0; j < kCpl; ++j) {
-        const int c = lane + j * kWave;
+        const int c = chunk(j);
         if (c < chunks) v[j] = load16_nt(permuted + int64_t(row[k]) * H + c * 8);
       }
       uint16_t* drow = d_permuted + int64_t(row[k]) * H;
 #pragma unroll
       for (int j = 0; j < kCpl; ++j) {
-        const int c = lane + j * kWave;
+        const int c = chunk(j);
         if (c < chunks) {
           float f[8], gf[8];
           unpack8(v[j], f);
@@ -87,6 +95,12 @@ k_unpermute_grad(const uint16_t* __restrict__ grad_out, const uint16_t* __restri
       dot = wave_sum(dot);
     }
     if (lane == k) mine = dot;  // 0 for a slot without a row
+  }
+  if (nsplit > 1) {
+    if (part != 0 && lane < K) xch[w][lane] = mine;
+    __syncthreads();
+    if (part != 0 || !live) return;
+    if (lane < K) mine += xch[w + 1][lane];
   }
   if (lane < K) d_probs[t * K + lane] = mine;
 }
@@ -135,13 +149,16 @@ hipError_t launch_unpermute_grad(const uint16_t* grad_out, const uint16_t* permu
                                  const int32_t* row_of_slot, const float* probs, int64_t T, int K,
                                  int H, uint16_t* d_permuted, float* d_probs, hipStream_t st) {
   if (T == 0) return hipGetLastError();
-  const dim3 grid(static_cast<unsigned>(ceil_div(T, kWaves)));
+  // two waves per token for long rows below 2 * kSplitBelowTokens tokens: the
+  // register-resident row halves, so occupancy doubles
+  const int nsplit = (H / 8 >= 4 * kWave && T < 2 * kSplitBelowTokens) ? 2 : 1;
+  const dim3 grid(static_cast<unsigned>(ceil_div(T, kWaves / nsplit)));
   const dim3 block(kWaves * kWave);
-  const int cpl = static_cast<int>(ceil_div(H / 8, kWave));
+  const int cpl = static_cast<int>(ceil_div(H / 8, kWave * nsplit));
 #define MOE_GRAD_CASE(C)                                                                        \
   if (cpl <= C) {                                                                               \
     hipLaunchKernelGGL(k_unpermute_grad<C>, grid, block, 0, st, grad_out, permuted, N,          \
-                       row_of_slot, probs, T, K, H, d_permuted, d_probs);                       \
+                       row_of_slot, probs, T, K, H, d_permuted, d_probs, nsplit);               \
     return hipGetLastError();                                                                   \
   }
   MOE_GRAD_CASE(1)
@@ -150,7 +167,8 @@ hipError_t launch_unpermute_grad(const uint16_t* grad_out, const uint16_t* permu
   MOE_GRAD_CASE(8)
   MOE_GRAD_CASE(16)
 #undef MOE_GRAD_CASE
-  hipLaunchKernelGGL(k_unpermute_grad_any, grid, block, 0, st, grad_out, permuted, N, row_of_slot,
+  hipLaunchKernelGGL(k_unpermute_grad_any, dim3(static_cast<unsigned>(ceil_div(T, kWaves))), block,
+                     0, st, grad_out, permuted, N, row_of_slot,
                      probs, T, K, H, d_permuted, d_probs);
   return hipGetLastError();
 }

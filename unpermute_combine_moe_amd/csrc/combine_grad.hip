@@ -125,7 +125,7 @@ k_combine_grad(const uint16_t* __restrict__ grad_out, const uint16_t* __restrict
           for (int i = 0; i < 4; ++i)
             d.w[i] = mul_to_bf16_exact(p[k], g[2 * i]) |
                      (mul_to_bf16_exact(p[k], g[2 * i + 1]) << 16);
-          store16_nt(o.d_expert_out + int64_t(src[k]) * H + h0, d);
+          store16(o.d_expert_out + int64_t(src[k]) * H + h0, d);
         }
       } else if (kind[k] == kCopy) {
 #pragma unroll
@@ -156,7 +156,7 @@ k_combine_grad(const uint16_t* __restrict__ grad_out, const uint16_t* __restrict
         }
       }
     }
-    if (o.d_ori_x != nullptr) store16_nt(o.d_ori_x + t * H + h0, pack8(dori));
+    if (o.d_ori_x != nullptr) store16(o.d_ori_x + t * H + h0, pack8(dori));
   }
 
   // per-slot sums across the wave, then across the token's waves (the

@@ -438,7 +438,19 @@ def cpu_baseline(d, n_tok):
             "kind": "oracle",
             "sample": f"first {n_tok} of {c['T']} tokens of the layer workload "
                       f"({n_tok * c['K']} routed rows), same step: permute, fp64 SwiGLU FFN, "
-                      f"combine, combine backward; {el:.1f} s on {platform.processor() or 'host'}"}
+                      f"combine, combine backward; {el:.1f} s on {cpu_model()} "
+                      f"({os.cpu_count()} logical CPUs visible, OMP_NUM_THREADS="
+                      f"{os.environ.get('OMP_NUM_THREADS', 'unset')})"}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "host"
 
 
 # ----------------------------------------------------------------------------- main
@@ -483,7 +495,11 @@ def main():
                 "traffic": rec["traffic_bytes"] if rec else None,
                 "avg_us": round(g_us, 2), "flops_per_launch": gemm_flops(n_rows, H, I),
                 "algorithmic_bytes_per_launch": gemm_bytes(n_rows, H, I, active),
-                "hbm_gbs_algorithmic": round(gemm_bytes(n_rows, H, I, active) / (g_us * 1e-6) / 1e9, 1)}
+                "hbm_gbs_algorithmic": round(gemm_bytes(n_rows, H, I, active) / (g_us * 1e-6) / 1e9, 1),
+                # the call's own roofline time, max(F / peak, bytes / 8 TB/s), over its time
+                "attainable_frac": round(max(gemm_flops(n_rows, H, I) / (BF16_DENSE_PEAK_TFLOPS * 1e12),
+                                             gemm_bytes(n_rows, H, I, active) / (HBM_PEAK_GBS * 1e9))
+                                         / (g_us * 1e-6), 4)}
     # per-op figures of the layer's memory-bound calls: each call timed alone with
     # a 1 GiB write between launches (nothing left in the 256 MB Infinity Cache);
     # with --no-ops, the in-step times instead (marked as such)

@@ -36,6 +36,7 @@ def _run_and_compare(moe, x, ids, E, rows=True):
     (3000, 8, 256, 64, 5, 4),     # special ids >= E mixed in
     (777, 16, 40, 32, 3, 5),      # K = 16
     (2049, 1, 1024, 8, 0, 6),     # E = 1024
+    (8192, 4, 1024, 8, 0, 8),     # E = 1024 with a full count table (scan LDS past 64 KB)
     (4097, 4, 17, 8, 2, 7),
 ])
 def test_permute_random(moe_lib, T, K, E, H, special, seed):

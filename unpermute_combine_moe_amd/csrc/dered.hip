@@ -27,6 +27,7 @@ namespace {
 constexpr int kSetupThreads = 1024;
 constexpr int kIndexThreads = 256;
 constexpr int kRowWaves = 4;
+constexpr int kWbBatch = 4;  // 16-byte chunks per lane loaded before their stores
 
 // ws layout (int32): flat[oep*E] | blk_start[B] | blk_cnt[B] | blk_dst[B] | total[1]
 __global__ void __launch_bounds__(kSetupThreads)
@@ -142,14 +143,26 @@ k_whiteboard_rows(const uint16_t* __restrict__ src, const float* __restrict__ co
     return;
   }
   const float p = coeff[j];
-  for (int c = lane; c < chunks; c += kWave) {
-    float f[8];
-    unpack8(load16_nt(s + c * 8), f);
-    Vec8 d;
+  // kWbBatch chunks per lane: all loads issued before their stores
+  for (int c0 = lane; c0 < chunks; c0 += kWave * kWbBatch) {
+    Vec8 v[kWbBatch];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      d.w[i] = scaled_bf16(p, f[2 * i]) | (scaled_bf16(p, f[2 * i + 1]) << 16);
-    store16_nt(dst + c * 8, d);
+    for (int b = 0; b < kWbBatch; ++b) {
+      const int c = c0 + b * kWave;
+      if (c < chunks) v[b] = load16_nt(s + c * 8);
+    }
+#pragma unroll
+    for (int b = 0; b < kWbBatch; ++b) {
+      const int c = c0 + b * kWave;
+      if (c >= chunks) continue;
+      float f[8];
+      unpack8(v[b], f);
+      Vec8 d;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        d.w[i] = scaled_bf16(p, f[2 * i]) | (scaled_bf16(p, f[2 * i + 1]) << 16);
+      store16_nt(dst + c * 8, d);
+    }
   }
 }
 

@@ -240,6 +240,7 @@ k_route_empty(int E, int32_t* __restrict__ counts, int32_t* __restrict__ offsets
 // Row copy, token-major: each wave reads its token's row once and writes it to
 // the K rows the token's slots landed on (16-byte vectors, coalesced).
 constexpr int kRowWaves = 4;
+constexpr int kRowBatch = 4;  // 16-byte chunks per lane loaded before their stores
 __global__ void __launch_bounds__(kRowWaves * kWave)
 k_permute_rows(const uint16_t* __restrict__ x, const int32_t* __restrict__ row_of_slot,
                int64_t T, int H, int K, int64_t S, uint16_t* __restrict__ permuted, int nsplit) {
@@ -254,11 +255,24 @@ k_permute_rows(const uint16_t* __restrict__ x, const int32_t* __restrict__ row_o
   for (int k = 0; k < 16; ++k) rows[k] = (k < K) ? row_of_slot[t * K + k] : -1;
   const int chunks = H / 8;
   const uint16_t* src = x + t * H;
-  for (int c = lane + part * kWave; c < chunks; c += kWave * nsplit) {
-    const Vec8 v = load16_nt(src + c * 8);
+  // kRowBatch chunks per lane: all loads issued before their stores
+  const int step = kWave * nsplit;
+  for (int c0 = lane + part * kWave; c0 < chunks; c0 += step * kRowBatch) {
+    Vec8 v[kRowBatch];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      if (k < K && rows[k] >= 0 && rows[k] < S) store16(permuted + int64_t(rows[k]) * H + c * 8, v);
+    for (int b = 0; b < kRowBatch; ++b) {
+      const int c = c0 + b * step;
+      if (c < chunks) v[b] = load16_nt(src + c * 8);
+    }
+#pragma unroll
+    for (int b = 0; b < kRowBatch; ++b) {
+      const int c = c0 + b * step;
+      if (c >= chunks) continue;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        if (k < K && rows[k] >= 0 && rows[k] < S)
+          store16(permuted + int64_t(rows[k]) * H + c * 8, v[b]);
+      }
     }
   }
 }

@@ -19,6 +19,7 @@ namespace {
 constexpr int kSetupThreads = 1024;
 constexpr int kRowsPerWg = 32;
 constexpr int kRowThreads = 256;
+constexpr int kCopyBatch = 8;  // 16-byte chunks per lane in flight in the row copy
 
 // ws layout (int32): src_rm[B] | cnt_em[B] | src_em[B] | dst_em[B] | total[1]
 __global__ void __launch_bounds__(kSetupThreads)
@@ -103,7 +104,20 @@ k_reorder_rows(const uint16_t* __restrict__ x, const int32_t* __restrict__ ws, i
     if (i >= N || src < 0) continue;
     const uint16_t* s = x + int64_t(src) * H;
     uint16_t* d = y + i * H;
-    for (int c = lane; c < chunks; c += kWave) store16_nt(d + c * 8, load16_nt(s + c * 8));
+    // a batch of kCopyBatch chunks per lane: all loads issued, then all stores
+    for (int c0 = lane; c0 < chunks; c0 += kWave * kCopyBatch) {
+      Vec8 v[kCopyBatch];
+#pragma unroll
+      for (int b = 0; b < kCopyBatch; ++b) {
+        const int c = c0 + b * kWave;
+        if (c < chunks) v[b] = load16_nt(s + c * 8);
+      }
+#pragma unroll
+      for (int b = 0; b < kCopyBatch; ++b) {
+        const int c = c0 + b * kWave;
+        if (c < chunks) store16_nt(d + c * 8, v[b]);
+      }
+    }
   }
 }
 

@@ -27,7 +27,8 @@ enum SlotKind : int { kDrop = 0, kRow = 1, kCopy = 2, kConst = 3 };
 // otherwise they are one pair per (token, const expert), read with the slot
 // metadata. kUnit: the permute backward -- every slot with a row has weight
 // 1 and there are no ids, special experts or shared term.
-template <bool kHasRowMap, bool kAlphaPerH, bool kUnit = false>
+// kMaxK: the slot arrays are sized for K <= kMaxK (8 or 16).
+template <bool kHasRowMap, bool kAlphaPerH, bool kUnit, int kMaxK>
 __global__ void __launch_bounds__(kWaves * kWave)
 k_combine(const uint16_t* __restrict__ expert_out, int64_t N, const int32_t* __restrict__ row_of_slot,
           const int32_t* __restrict__ row_map, const int32_t* __restrict__ ids,
@@ -80,11 +81,11 @@ k_combine(const uint16_t* __restrict__ expert_out, int64_t N, const int32_t* __r
       }
     }
   }
-  int kind[16], src[16];
-  float p[16], a1[16], a2[16];
+  int kind[kMaxK], src[kMaxK];
+  float p[kMaxK], a1[kMaxK], a2[kMaxK];
   bool need_ori = false;
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
+  for (int k = 0; k < kMaxK; ++k) {
     kind[k] = k < K ? __builtin_amdgcn_readlane(m_kind, k) : kDrop;
     src[k] = __builtin_amdgcn_readlane(m_src, k);
     p[k] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(m_p), k));
@@ -101,14 +102,14 @@ k_combine(const uint16_t* __restrict__ expert_out, int64_t N, const int32_t* __r
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.f;
     // loads of the routed rows first, so they are all in flight together
-    Vec8 v[16];
+    Vec8 v[kMaxK];
 #pragma unroll
-    for (int k = 0; k < 16; ++k)
+    for (int k = 0; k < kMaxK; ++k)
       if (kind[k] == kRow) v[k] = load16_nt(expert_out + int64_t(src[k]) * H + h0);
     float o[8];
     if (need_ori) unpack8(load16(orow + h0), o);
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
+    for (int k = 0; k < kMaxK; ++k) {
       if (kind[k] == kRow) {
         float f[8];
         unpack8(v[k], f);
@@ -162,15 +163,23 @@ hipError_t launch_combine(const uint16_t* expert_out, int64_t N, const int32_t* 
   const dim3 grid(static_cast<unsigned>(ceil_div(T, kWaves / nsplit)));
   const dim3 block(kWaves * kWave);
   const bool per_h = sp.num_const > 0 && sp.a_sh != 0;
-#define MOE_COMBINE(RM, PH)                                                                    \
-  hipLaunchKernelGGL((k_combine<RM, PH>), grid, block, 0, st, expert_out, N, row_of_slot,     \
-                     row_map, ids, probs, mk, T, K, H, E, sp, shared_x, out, nsplit)
+#define MOE_COMBINE_K(RM, PH, MK)                                                              \
+  hipLaunchKernelGGL((k_combine<RM, PH, false, MK>), grid, block, 0, st, expert_out, N,       \
+                     row_of_slot, row_map, ids, probs, mk, T, K, H, E, sp, shared_x, out, nsplit)
+#define MOE_COMBINE(RM, PH) \
+  {                                 \
+    if (K <= 8)                     \
+      MOE_COMBINE_K(RM, PH, 8);     \
+    else                            \
+      MOE_COMBINE_K(RM, PH, 16);    \
+  }
   if (row_map != nullptr) {
-    if (per_h) MOE_COMBINE(true, true); else MOE_COMBINE(true, false);
+    if (per_h) MOE_COMBINE(true, true) else MOE_COMBINE(true, false)
   } else {
-    if (per_h) MOE_COMBINE(false, true); else MOE_COMBINE(false, false);
+    if (per_h) MOE_COMBINE(false, true) else MOE_COMBINE(false, false)
   }
 #undef MOE_COMBINE
+#undef MOE_COMBINE_K
   return hipGetLastError();
 }
 
@@ -180,9 +189,14 @@ hipError_t launch_permute_grad(const uint16_t* d_permuted, int64_t N, const int3
   const int nsplit = split_for(T, H);
   const dim3 grid(static_cast<unsigned>(ceil_div(T, kWaves / nsplit)));
   const dim3 block(kWaves * kWave);
-  hipLaunchKernelGGL((k_combine<false, false, true>), grid, block, 0, st, d_permuted, N,
-                     row_of_slot, nullptr, nullptr, nullptr, SlotMask{nullptr, 0, K}, T, K, H, 0,
-                     SpecialArgs{}, nullptr, d_x, nsplit);
+  if (K <= 8)
+    hipLaunchKernelGGL((k_combine<false, false, true, 8>), grid, block, 0, st, d_permuted, N,
+                       row_of_slot, nullptr, nullptr, nullptr, SlotMask{nullptr, 0, K}, T, K, H,
+                       0, SpecialArgs{}, nullptr, d_x, nsplit);
+  else
+    hipLaunchKernelGGL((k_combine<false, false, true, 16>), grid, block, 0, st, d_permuted, N,
+                       row_of_slot, nullptr, nullptr, nullptr, SlotMask{nullptr, 0, K}, T, K, H,
+                       0, SpecialArgs{}, nullptr, d_x, nsplit);
   return hipGetLastError();
 }
 

@@ -32,9 +32,11 @@ enum SlotKind : int { kDrop = 0, kRow = 1, kCopy = 2, kConst = 3 };
 
 // kAlphaPerH: the const-expert coefficients vary along h (stride_h != 0).
 // kMaxK: the slot arrays are sized for K <= kMaxK (8 or 16), so that the
-// common K <= 8 keeps half the registers.
+// common K <= 8 keeps half the registers; there the kernel is held to four
+// waves per SIMD (at most 128 VGPRs, which it fits without spilling).
 template <bool kHasRowMap, bool kAlphaPerH, int kMaxK>
 __global__ void __launch_bounds__(kWaves * kWave)
+__attribute__((amdgpu_waves_per_eu(kMaxK <= 8 ? 4 : 1)))
 k_combine_grad(const uint16_t* __restrict__ grad_out, const uint16_t* __restrict__ expert_out,
                int64_t N, const int32_t* __restrict__ row_of_slot,
                const int32_t* __restrict__ row_map, const int32_t* __restrict__ ids,

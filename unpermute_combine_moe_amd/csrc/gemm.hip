@@ -35,6 +35,12 @@
 // index (A: by (row / 2) & 7, B: by 4 * (k & 3)) that keeps the operand reads free of
 // bank conflicts; the swizzle is applied by choosing which global chunk each
 // lane loads, since a direct-to-LDS load writes lane L at base + 16 L.
+//
+// Epilogue: the output fragments are staged in LDS (in the ring stage that the
+// tile's last k-step has just freed) and written back row-contiguous with
+// 16-byte buffer stores, so each store covers whole 128-byte lines; stores of
+// padding rows carry an offset past the tile's valid rows and are dropped by
+// the buffer range check.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -43,6 +49,7 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int BM = 128;
 constexpr int BN = 256;  // B-columns per tile
@@ -101,13 +108,32 @@ constexpr int kLoadsA = kChunksA / kThreads;  // direct-to-LDS loads per thread 
 constexpr int kLoadsB = kChunksB / kThreads;
 constexpr int kLoadsPerStage = kLoadsA + kLoadsB;
 constexpr int kStageBytes = (kChunksA + kChunksB) * 16;
-// epilogue stores per wave per tile: 2 row fragments x output fragments x 4
-// (x 2 in mode 2, which writes dg and du)
+// Epilogue. Each 32-row fragment of a wave's output goes through LDS: the
+// lanes write their MFMA results (one token row per lane, four consecutive
+// columns per register group) as packed bf16, then read the fragment back
+// row-contiguous, 16 bytes per lane, and store it so that one store covers
+// whole rows (4 rows x 256 B or 8 rows x 128 B) instead of 32 rows x 16 B.
+// kRowBytes: bytes of one staged row (the wave's output columns; mode 2 puts
+// dg and du side by side); 16-byte chunks are XOR-swizzled by row so that
+// both the column-wise writes and the row-wise reads are free of bank
+// conflicts. kStores counts the vector-memory stores a wave issues per tile.
 template <int kMode>
 struct EpiloguePlan {
   static constexpr int kOutFrags = (kMode == 1) ? 4 : 2;
-  static constexpr int kStores = 2 * kOutFrags * 4 * (kMode == 2 ? 2 : 1);
+  static constexpr int kRowBytes = (kMode == 0) ? 128 : 256;
+  static constexpr int kChunks = kRowBytes / 16;        // per staged row
+  static constexpr int kRowsPerStore = kWave / kChunks;  // rows one wave-wide store covers
+  static constexpr int kStoresPerFrag = 32 / kRowsPerStore;
+  static constexpr int kStores = 2 * kStoresPerFrag;
+  static constexpr int kWaveBytes = 32 * kRowBytes;     // staging area of one wave
 };
+
+template <int kRowBytes>
+__device__ __forceinline__ int stage_chunk(int row, int chunk) {
+  // rows of 256 B start on the same bank: key = row % 16; rows of 128 B
+  // alternate between the two bank halves: key = (row / 2) % 8
+  return kRowBytes == 256 ? (chunk ^ (row & 15)) : (chunk ^ ((row >> 1) & 7));
+}
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
@@ -139,6 +165,12 @@ __device__ __forceinline__ void reads_done_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Wait until this wave's own LDS accesses have completed.
+__device__ __forceinline__ void wait_lds_reads() {
+  // lgkmcnt(0); vmcnt (63) and expcnt (7) unconstrained
+  __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
+}
+
 __device__ __forceinline__ int swz_b(int k, int c) { return k * (BN / 8) + (c ^ (4 * (k & 3))); }
 
 __device__ __forceinline__ bf16x8_t lds_read_a(const lds_u8_t* base, int slot) {
@@ -156,7 +188,7 @@ template <int kMode>
 __global__ void __launch_bounds__(kThreads, 1)
 k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0,
        const uint16_t* __restrict__ B1, int Ncols, const int32_t* __restrict__ ws, int E,
-       uint16_t* __restrict__ C, uint2* __restrict__ trash, const uint16_t* __restrict__ aux) {
+       uint16_t* __restrict__ C, const uint16_t* __restrict__ aux) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes];
   // row-tile prefix and clamped expert offsets, staged once per workgroup so the
   // per-tile expert lookup is a binary search in LDS
@@ -398,59 +430,100 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
     }
 
     epi_step = s - 1;
+    {
+      using EP = EpiloguePlan<kMode>;
+      static_assert(4 * EP::kWaveBytes <= kStageBytes, "staging fits one ring stage");
+      // Staging space: the ring stage of step s - 1, which every wave has
+      // finished reading (the barrier of that step's last sub-step) and which
+      // is refilled only by stage s + 2's loads, issued during step s after
+      // the barrier at the end of this epilogue.
+      lds_u8_t* stg = lds + ((cbuf + kStages - 1) % kStages) * kStageBytes + wave * EP::kWaveBytes;
+      constexpr int ldc = (kMode == 2) ? 2 : 1;  // C row stride in units of Ncols
+      // Buffer stores: a store whose offset lies past the tile's last valid
+      // row is dropped by the hardware, so padding rows need no branch and
+      // every lane issues every store (the vmcnt waits count them).
+      const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+          C + int64_t(ci.row0) * Ncols * ldc, 0, (ci.row_end - ci.row0) * Ncols * ldc * 2,
+          0x00020000);
+      const int wcol0 = ci.n0 + ((kMode == 1) ? wn * 128 : wn * 64);  // wave's first output column
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int row = ci.row0 + wm * 64 + i * 32 + lane % 32;
-      const bool row_ok = row < ci.row_end;
-      constexpr int kOutFrags = EpiloguePlan<kMode>::kOutFrags;
-      constexpr int64_t ldc = (kMode == 2) ? 2 : 1;
-      uint16_t* crow = C + int64_t(row_ok ? row : 0) * Ncols * ldc;
+      for (int i = 0; i < 2; ++i) {
+        const int r = lane % 32;  // this lane's row in the fragment
+        const int row = ci.row0 + wm * 64 + i * 32 + r;
 #pragma unroll
-      for (int jj = 0; jj < kOutFrags; ++jj) {
+        for (int jj = 0; jj < EP::kOutFrags; ++jj) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = ci.n0 + ((kMode == 1) ? wn * 128 : wn * 64) + jj * 32 + 8 * q +
-                          4 * (lane / 32);
-          const bool ok = row_ok && col < Ncols;
-          float v[4], w[4];
-          float d[4] = {0.f, 0.f, 0.f, 0.f};
-          if (kMode == 2 && ok) {
-            const uint2 dh = *reinterpret_cast<const uint2*>(aux + int64_t(row) * Ncols + col);
-            d[0] = bf16_lo(dh.x);
-            d[1] = bf16_hi(dh.x);
-            d[2] = bf16_lo(dh.y);
-            d[3] = bf16_hi(dh.y);
-          }
+          for (int q = 0; q < 4; ++q) {
+            const int col = wcol0 + jj * 32 + 8 * q + 4 * (lane / 32);
+            float v[4], w[4];
+            float d[4] = {0.f, 0.f, 0.f, 0.f};
+            if (kMode == 2 && row < ci.row_end && col < Ncols) {
+              const uint2 dh = *reinterpret_cast<const uint2*>(aux + int64_t(row) * Ncols + col);
+              d[0] = bf16_lo(dh.x);
+              d[1] = bf16_hi(dh.x);
+              d[2] = bf16_lo(dh.y);
+              d[3] = bf16_hi(dh.y);
+            }
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            if (kMode == 0) {
-              const float g = acc[i][jj][4 * q + k];
-              const float u = acc[i][jj + 2][4 * q + k];
-              v[k] = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
-            } else if (kMode == 2) {
-              const float g = acc[i][jj][4 * q + k];
-              const float u = acc[i][jj + 2][4 * q + k];
-              const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g));
-              v[k] = d[k] * u * sg * (1.0f + g * (1.0f - sg));  // dg
-              w[k] = d[k] * g * sg;                              // du
-            } else {
-              v[k] = acc[i][jj][4 * q + k];
+            for (int k = 0; k < 4; ++k) {
+              if (kMode == 0) {
+                const float g = acc[i][jj][4 * q + k];
+                const float u = acc[i][jj + 2][4 * q + k];
+                v[k] = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+              } else if (kMode == 2) {
+                const float g = acc[i][jj][4 * q + k];
+                const float u = acc[i][jj + 2][4 * q + k];
+                const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+                v[k] = d[k] * u * sg * (1.0f + g * (1.0f - sg));  // dg
+                w[k] = d[k] * g * sg;                              // du
+              } else {
+                v[k] = acc[i][jj][4 * q + k];
+              }
+            }
+            // chunk of these four columns in the staged row, and which half of it
+            const int chunk = 4 * jj + q;
+            const u32x2_t pv = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+            *reinterpret_cast<__attribute__((address_space(3))) u32x2_t*>(
+                stg + r * EP::kRowBytes + stage_chunk<EP::kRowBytes>(r, chunk) * 16 +
+                (lane / 32) * 8) = pv;
+            if (kMode == 2) {  // du in the second half of the staged row
+              const u32x2_t pw = {pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3])};
+              *reinterpret_cast<__attribute__((address_space(3))) u32x2_t*>(
+                  stg + r * EP::kRowBytes + stage_chunk<EP::kRowBytes>(r, 8 + chunk) * 16 +
+                  (lane / 32) * 8) = pw;
             }
           }
-          uint2 packed;
-          packed.x = pack_bf16x2(v[0], v[1]);
-          packed.y = pack_bf16x2(v[2], v[3]);
-          uint2* dst = ok ? reinterpret_cast<uint2*>(crow + col) : trash + lane;
-          *dst = packed;
+        }
+        // this wave's writes have landed before it reads them back (the
+        // staging area is private to the wave)
+        wait_lds_reads();
+#pragma unroll
+        for (int t = 0; t < EP::kStoresPerFrag; ++t) {
+          const int rr = t * EP::kRowsPerStore + lane / EP::kChunks;
+          const int c = lane % EP::kChunks;
+          const u32x4_t val = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(
+              stg + rr * EP::kRowBytes + stage_chunk<EP::kRowBytes>(rr, c) * 16);
+          const int lrow = wm * 64 + i * 32 + rr;  // row within the tile
+          int col, dst_col;
           if (kMode == 2) {
-            uint2 pw;
-            pw.x = pack_bf16x2(w[0], w[1]);
-            pw.y = pack_bf16x2(w[2], w[3]);
-            uint2* dw = ok ? reinterpret_cast<uint2*>(crow + Ncols + col) : trash + lane;
-            *dw = pw;
+            col = wcol0 + (c % 8) * 8;
+            dst_col = (c < 8) ? col : Ncols + col;
+          } else {
+            col = wcol0 + c * 8;
+            dst_col = col;
           }
+          const bool ok = ci.row0 + lrow < ci.row_end && col < Ncols;
+          const int off = ok ? (lrow * Ncols * ldc + dst_col) * 2 : 0x80000000;
+          // h and [dg | du] non-temporal (so they do not displace the operand
+          // panels in L2); y plain, since the combine that follows reads it
+          // back and finds it in the caches
+          __builtin_amdgcn_raw_buffer_store_b128(val, rsrc, off, 0, kMode == 1 ? 0 : /*nt*/ 2);
         }
       }
+      // every wave has read its staged rows before stage s + 2's loads refill
+      // this ring stage
+      wait_lds_reads();
+      stage_barrier();
     }
   }
 }
@@ -467,12 +540,9 @@ int persistent_grid() {
 
 }  // namespace
 
-// ws layout: tile_prefix[E+1] | offs[E+1] (int32), then at kTrashOffset(E) a
-// 512-byte area that absorbs the epilogue stores of lanes without a valid row
-size_t trash_offset(int E) { return ((static_cast<size_t>(2 * (E + 1)) * 4 + 255) / 256) * 256; }
-
+// ws layout: tile_prefix[E+1] | offs[E+1] (int32)
 size_t gemm_workspace_bytes(int E, int64_t /*N_cap*/, int /*H*/, int /*I*/) {
-  return trash_offset(E) + kWave * 8;
+  return ((static_cast<size_t>(2 * (E + 1)) * 4 + 255) / 256) * 256;
 }
 
 hipError_t launch_grouped_gemm_swiglu(const uint16_t* x, const int32_t* offsets, int E,
@@ -483,18 +553,16 @@ hipError_t launch_grouped_gemm_swiglu(const uint16_t* x, const int32_t* offsets,
   hipLaunchKernelGGL(k_gemm_sched, dim3(1), dim3(kSchedThreads), 0, st, offsets, E, N_cap, w);
   if (N_cap == 0) return hipGetLastError();
   const int G = persistent_grid();
-  uint2* trash = reinterpret_cast<uint2*>(static_cast<char*>(ws) + trash_offset(E));
-  hipLaunchKernelGGL(k_gemm<0>, dim3(G), dim3(kThreads), 0, st, x, H, wg, wu, I, w, E, h, trash,
-                     nullptr);
+  hipLaunchKernelGGL(k_gemm<0>, dim3(G), dim3(kThreads), 0, st, x, H, wg, wu, I, w, E, h, nullptr);
   hipLaunchKernelGGL(k_gemm<1>, dim3(G), dim3(kThreads), 0, st, h, I, wd, nullptr, H, w, E, y,
-                     trash, nullptr);
+                     nullptr);
   return hipGetLastError();
 }
 
 // Backward: dh = dy Wd^T (row-grouped), [dg | du] from the recomputed gate/up
 // tiles (mode 2), dx = [dg | du] [Wg ; Wu]^T (row-grouped), dWd = h^T dy and
 // [dWg | dWu] = x^T [dg | du] (sums over each expert's rows).
-// ws layout: forward tables (trash included) | backward tables | zeros[256 B]
+// ws layout: forward tables | backward tables | zeros[256 B]
 //            | dh [N_cap, I] bf16 | dgu [N_cap, 2I] bf16
 size_t gemm_grad_layout(int E, int64_t N_cap, int I, size_t* off_bt, size_t* off_zero,
                         size_t* off_dh, size_t* off_dgu) {
@@ -531,7 +599,6 @@ hipError_t launch_grouped_gemm_swiglu_grad(const uint16_t* x, const int32_t* off
   uint16_t* zeros = reinterpret_cast<uint16_t*>(base + off_zero);
   uint16_t* dh = reinterpret_cast<uint16_t*>(base + off_dh);
   uint16_t* dgu = reinterpret_cast<uint16_t*>(base + off_dgu);
-  uint2* trash = reinterpret_cast<uint2*>(base + trash_offset(E));
   hipLaunchKernelGGL(k_fill_zero, dim3(1), dim3(64), 0, st, reinterpret_cast<uint32_t*>(zeros), 64);
   hipLaunchKernelGGL(k_gemm_sched, dim3(1), dim3(kSchedThreads), 0, st, offsets, E, N_cap, w);
   hipError_t err = launch_bgemm_sched(offsets, E, N_cap, bt, st);
@@ -542,8 +609,7 @@ hipError_t launch_grouped_gemm_swiglu_grad(const uint16_t* x, const int32_t* off
     if (err != hipSuccess) return err;
     // [dg | du] from the recomputed gate and up tiles
     const int G = persistent_grid();
-    hipLaunchKernelGGL(k_gemm<2>, dim3(G), dim3(kThreads), 0, st, x, H, wg, wu, I, w, E, dgu,
-                       trash, dh);
+    hipLaunchKernelGGL(k_gemm<2>, dim3(G), dim3(kThreads), 0, st, x, H, wg, wu, I, w, E, dgu, dh);
     // dx = [dg | du] [Wg ; Wu]^T: B_e = Wg[e], Wu[e] as [H][I] side by side along k
     err = launch_bgemm_rows(dgu, 2 * I, wg, wu, I, I, int64_t(H) * I, H, N_cap, bt, E, dx, st);
     if (err != hipSuccess) return err;

@@ -83,28 +83,45 @@ __device__ __forceinline__ void st_lds16(lds_u8_t* t, int slot, const uint4& v) 
   *(__attribute__((address_space(3))) u32x4_t*)(t + slot * 16) = u;
 }
 
-// Stores of one wave's 64 x 64 accumulator block: row m = m0 + 32 i + lane % 32,
-// four consecutive columns n = n0 + 32 j + 8 q + 4 (lane / 32) per 8-byte store.
-// Columns at or past `split` go to C1 at column n - split.
-__device__ __forceinline__ void store_block(const f32x16_t acc[2][2], int m0, int m_end, int n0,
-                                            int n_end, int split, uint16_t* C0, uint16_t* C1,
-                                            int64_t ldc, int lane) {
+// Stores of one wave's 64 x 64 accumulator block, rows m0 .. m0 + 63 and
+// columns n0 .. n0 + 63 (columns at or past `split` go to C1 at column
+// n - split; rows >= m_end and columns >= n_end are not stored). In registers
+// a lane holds row m0 + 32 i + lane % 32 and four consecutive columns
+// n0 + 32 j + 8 q + 4 (lane / 32), so a direct store would cover 32 rows x 16 B.
+// The block goes through the wave's 8 KB staging area `stg` in LDS as
+// [64 rows][128 B] (16-byte chunks XOR-swizzled by (row / 2) % 8, which keeps
+// both the column-wise writes and the row-wise reads free of bank conflicts)
+// and is written back 16 B per lane, 8 rows x 128 B per store.
+__device__ __forceinline__ void store_block(const f32x16_t acc[2][2], lds_u8_t* stg, int m0,
+                                            int m_end, int n0, int n_end, int split,
+                                            uint16_t* C0, uint16_t* C1, int64_t ldc, int lane) {
+  typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int m = m0 + 32 * i + lane % 32;
-    if (m >= m_end) continue;
+    const int r = 32 * i + lane % 32;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int n = n0 + 32 * j + 8 * q + 4 * (lane / 32);
-        if (n >= n_end) continue;
-        uint2 packed;
-        packed.x = pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]);
-        packed.y = pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-        uint16_t* dst = n < split ? C0 + int64_t(m) * ldc + n : C1 + int64_t(m) * ldc + (n - split);
-        *reinterpret_cast<uint2*>(dst) = packed;
+        const u32x2_t packed = {pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                                pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
+        const int chunk = (4 * j + q) ^ ((r >> 1) & 7);
+        *reinterpret_cast<__attribute__((address_space(3))) u32x2_t*>(
+            stg + r * 128 + chunk * 16 + (lane / 32) * 8) = packed;
       }
+  }
+  // the wave's own writes have completed before it reads them back
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int r = 8 * t + lane / 8, c = lane % 8;
+    const u32x4_t v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(
+        stg + r * 128 + (c ^ ((r >> 1) & 7)) * 16);
+    const int m = m0 + r, n = n0 + 8 * c;
+    if (m < m_end && n < n_end) {
+      uint16_t* dst = n < split ? C0 + int64_t(m) * ldc + n : C1 + int64_t(m) * ldc + (n - split);
+      *reinterpret_cast<u32x4_t*>(dst) = v;
+    }
   }
 }
 
@@ -239,7 +256,9 @@ k_bgemm_rows(const uint16_t* __restrict__ A, int K, const uint16_t* __restrict__
     if (ks + 1 < ksteps) stash(buf ^ 1);
     __syncthreads();
   }
-  store_block(acc, row0 + wm * 64, row_end, n0 + wn * 64, Ncols, Ncols, C, C, Ncols, lane);
+  // the LDS is free: every wave has passed the k-loop's last barrier
+  store_block(acc, lds + wave * 8192, row0 + wm * 64, row_end, n0 + wn * 64, Ncols, Ncols, C, C,
+              Ncols, lane);
 }
 
 // k-grouped C_e = A_e^T B_e over the rows of expert e: A rows [row][m] (lda),
@@ -335,7 +354,10 @@ k_bgemm_kgroup(const uint16_t* __restrict__ A, int64_t lda, int M, const uint16_
     __syncthreads();
   }
   const int64_t ebase = int64_t(e) * M * ldc;
-  store_block(acc, m0 + wm * 64, M, n0 + wn * 64, N, split, C0 + ebase, C1 + ebase, ldc, lane);
+  // the LDS is free: every wave has passed the k-loop's last barrier (or, for
+  // an expert without rows, never used it)
+  store_block(acc, lds + wave * 8192, m0 + wm * 64, M, n0 + wn * 64, N, split, C0 + ebase,
+              C1 + ebase, ldc, lane);
 }
 
 }  // namespace

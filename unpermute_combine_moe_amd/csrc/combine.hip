@@ -150,7 +150,13 @@ k_combine(const uint16_t* __restrict__ expert_out, int64_t N, const int32_t* __r
 
 // Two waves per token when there are too few tokens to give every SIMD
 // several rounds of waves and each row has at least two 64-chunk rows.
-int split_for(int64_t T, int H) { return (H / 8 >= 2 * kWave && T < kSplitBelowTokens) ? 2 : 1; }
+// Waves per token: below kSplitBelowTokens a batch gives too few waves to keep
+// every SIMD busy for several rounds, so long rows are shared by 4 waves (or 2).
+int split_for(int64_t T, int H) {
+  if (T >= kSplitBelowTokens) return 1;
+  if (H / 8 >= 4 * kWave) return 4;
+  return H / 8 >= 2 * kWave ? 2 : 1;
+}
 
 }  // namespace
 

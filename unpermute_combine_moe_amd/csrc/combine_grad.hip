@@ -42,8 +42,8 @@ k_combine_grad(const uint16_t* __restrict__ grad_out, const uint16_t* __restrict
                const int32_t* __restrict__ row_map, const int32_t* __restrict__ ids,
                const float* __restrict__ probs, SlotMask mk, int64_t T, int K, int H, int E,
                SpecialArgs sp, CombineGradArgs o, int alpha_token, int nsplit) {
-  // nsplit waves share a token, each taking every nsplit-th 64-chunk row of
-  // the hidden dim; their per-slot sums meet in LDS
+  // nsplit waves (1, 2 or 4) share a token, each taking every nsplit-th
+  // 64-chunk row of the hidden dim; their per-slot sums meet in LDS
   __shared__ float xch[kWaves][2][kMaxK];
   const int w = threadIdx.x / kWave;
   const int part = w % nsplit;
@@ -181,11 +181,12 @@ k_combine_grad(const uint16_t* __restrict__ grad_out, const uint16_t* __restrict
     }
     __syncthreads();
     if (part != 0 || !live) return;
+    for (int q = 1; q < nsplit; ++q)  // partners in part order
 #pragma unroll
-    for (int k = 0; k < kMaxK; ++k) {
-      r1[k] += xch[w + 1][0][k];
-      r2[k] += xch[w + 1][1][k];
-    }
+      for (int k = 0; k < kMaxK; ++k) {
+        r1[k] += xch[w + q][0][k];
+        r2[k] += xch[w + q][1][k];
+      }
   }
   float mine = 0.f;
   float pr1[kMaxK], pr2[kMaxK];
@@ -548,9 +549,12 @@ hipError_t launch_combine_grad(const uint16_t* grad_out, const uint16_t* expert_
   const bool per_h = sp.num_const > 0 && sp.a_sh != 0;
   const int alpha_token = want_alpha && lay == AlphaLayout::kPerToken;
   {
-    // two waves per token once a token's row is long and there are too few
-    // tokens to keep every SIMD busy for several rounds
-    const int nsplit = (H / 8 >= 2 * kWave && T < 2 * kSplitBelowTokens) ? 2 : 1;
+    // four (or two) waves per token once a token's row is long and there are
+    // too few tokens to keep every SIMD busy for several rounds
+    const int nsplit = T >= 2 * kSplitBelowTokens ? 1
+                       : H / 8 >= 4 * kWave       ? 4
+                       : H / 8 >= 2 * kWave       ? 2
+                                                  : 1;
     const dim3 grid(static_cast<unsigned>(ceil_div(T, kWaves / nsplit)));
     const dim3 block(kWaves * kWave);
 #define MOE_CGRAD(RM, PH, MK)                                                                  \

@@ -100,7 +100,8 @@ k_unpermute_grad(const uint16_t* __restrict__ grad_out, const uint16_t* __restri
     if (part != 0 && lane < K) xch[w][lane] = mine;
     __syncthreads();
     if (part != 0 || !live) return;
-    if (lane < K) mine += xch[w + 1][lane];
+    if (lane < K)
+      for (int q = 1; q < nsplit; ++q) mine += xch[w + q][lane];  // partners in part order
   }
   if (lane < K) d_probs[t * K + lane] = mine;
 }

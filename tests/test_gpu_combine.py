@@ -35,7 +35,8 @@ def _combine_both(moe, eo, ros, ids, probs, E, *, row_map=None, Z=0, C=0, Nc=0, 
     return bits(got), ref, ref64
 
 
-@pytest.mark.parametrize("T,E,H", [(1, 1, 8), (333, 7, 136), (2048, 64, 2048)])
+@pytest.mark.parametrize("T,E,H", [(1, 1, 8), (333, 7, 136), (2048, 64, 2048),
+                                   (901, 24, 2120)])  # 4 waves per token, 265 chunks: uneven parts
 def test_top1_roundtrip_bit_exact(moe_lib, T, E, H):
     rng = np.random.default_rng(T)
     x = W.normal_bf16(rng, (T, H))

@@ -88,6 +88,7 @@ def test_combine_grad_layouts(moe_lib, layout):
     (1, 1, 1, 8, 1, 2),            # one token, one slot
     (2000, 8, 32, 1160, 9, 3),     # several hidden tiles with a ragged tail, 3 const groups
     (777, 16, 40, 520, 5, 4),      # K = 16, many segments
+    (901, 8, 24, 2120, 3, 6),      # 4 waves per token, 265 chunks: uneven parts
 ])
 def test_combine_grad_shapes(moe_lib, T, K, E, H, NC, seed):
     for layout in ("per_token", "const_by_h"):

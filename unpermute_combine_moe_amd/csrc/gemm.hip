@@ -17,7 +17,7 @@
 // each wave owns 64 rows x 128 B-columns = 2 x 4 MFMA 32x32 accumulators. The
 // MFMA is fed the weight fragment as its first operand, i.e. it computes the
 // transposed tile, so that each lane ends up with four consecutive output
-// columns of one token row (8-byte stores in the epilogue).
+// columns of one token row (8-byte writes into the epilogue's LDS staging).
 // Pass 1 packs 128 gate columns and the matching 128 up columns into the 256
 // B-columns, so the SwiGLU epilogue finds g and u of an output element in the
 // same lane and register.
@@ -159,12 +159,6 @@ __device__ __forceinline__ void load_lds16(const void* gptr, uint32_t lds_base) 
 // LDS accesses across it.
 __device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// Same, after this wave's own LDS reads have returned (so a stage it has read
-// may be refilled by any wave once everyone is past the barrier).
-__device__ __forceinline__ void reads_done_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
 // Wait until this wave's own LDS accesses have completed.
 __device__ __forceinline__ void wait_lds_reads() {
   // lgkmcnt(0); vmcnt (63) and expcnt (7) unconstrained
@@ -255,11 +249,17 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
     const int tile = first + j * per_xcd;
     const int rt = tile / col_tiles;
     const int ct = tile - rt * col_tiles;
-    int lo = 0, hi = E;  // expert owning row tile rt: last e with prefix[e] <= rt
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (prefix[mid] <= rt) lo = mid; else hi = mid;
-    }
+    // Expert owning row tile rt: the last e < E with prefix[e] <= rt (prefix
+    // is non-decreasing and prefix[0] = 0, so the e that pass form a run from
+    // 0). Two wave-wide probes instead of a binary search: lane l tests
+    // e = 16 l (E <= 1024), then lanes 0..15 test the 16 e of the last block
+    // that passed; the highest passing lane of each ballot gives the answer.
+    const int e1 = 16 * lane;
+    const uint64_t b1 = __builtin_amdgcn_ballot_w64(e1 < E && prefix[e1] <= rt);
+    const int blk = 63 - __builtin_clzll(b1);
+    const int e2 = 16 * blk + (lane & 15);
+    const uint64_t b2 = __builtin_amdgcn_ballot_w64(lane < 16 && e2 < E && prefix[e2] <= rt);
+    const int lo = uniform(16 * blk + 63 - __builtin_clzll(b2));
     TileInfo t;
     t.e = lo;
     t.row0 = offs[lo] + (rt - prefix[lo]) * BM;
@@ -305,26 +305,18 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
       b_src[i] = base + int64_t(t.e) * Kdim * Ncols + int64_t(k) * Ncols + col;
     }
   };
-  // The 12 loads of a stage are issued in four groups of three, one group per
-  // MFMA sub-step, so their address work hides under the matrix ops.
-  constexpr int kLoadGroups = BK / 16;
-  constexpr int kLoadsPerGroup = kLoadsPerStage / kLoadGroups;
-  static_assert(kLoadsPerStage % kLoadGroups == 0, "load groups");
   uint32_t l_st = 0;
   auto issue_begin = [&]() {
     if (lk == 0) load_tile_sources(lj);
     l_st = uniform(static_cast<int>(lds0 + lbuf * kStageBytes + wave * kWave * 16));
   };
-  auto issue_group = [&](int grp) {
-#pragma unroll
-    for (int g = 0; g < kLoadsPerGroup; ++g) {
-      const int i = grp * kLoadsPerGroup + g;
-      if (i < kLoadsA)
-        load_lds16(a_src[i] + lk * BK, l_st + i * kThreads * 16);
-      else
-        load_lds16(b_src[i - kLoadsA] + int64_t(lk) * BK * Ncols,
-                   l_st + (kChunksA + (i - kLoadsA) * kThreads) * 16);
-    }
+  // load i (0 .. kLoadsPerStage - 1) of the stage being issued
+  auto load1 = [&](int i) {
+    if (i < kLoadsA)
+      load_lds16(a_src[i] + lk * BK, l_st + i * kThreads * 16);
+    else
+      load_lds16(b_src[i - kLoadsA] + int64_t(lk) * BK * Ncols,
+                 l_st + (kChunksA + (i - kLoadsA) * kThreads) * 16);
   };
   auto issue_end = [&]() {
     lbuf = (lbuf + 1 == kStages) ? 0 : lbuf + 1;
@@ -336,34 +328,35 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
   auto issue_next = [&]() {
     issue_begin();
 #pragma unroll
-    for (int grp = 0; grp < kLoadGroups; ++grp) issue_group(grp);
+    for (int i = 0; i < kLoadsPerStage; ++i) load1(i);
     issue_end();
   };
 
-  // operand fragments of one 16-wide k sub-step of the stage at `st`
-  auto read_frags = [&](const lds_u8_t* st, int kk, bf16x8_t fa[2], bf16x8_t fb[4]) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      fa[i] = lds_read_a(st, swz(wm * 64 + i * 32 + lane % 32, kk * 2 + lane / 32));
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const v4i16_t lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_v4i16_t*)(st + b_off[jj][0] + kk * 16 * (BN * 2)));
-      const v4i16_t hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_v4i16_t*)(st + b_off[jj][1] + kk * 16 * (BN * 2)));
-      __builtin_memcpy(&fb[jj], &lo4, 8);
-      __builtin_memcpy(reinterpret_cast<char*>(&fb[jj]) + 8, &hi4, 8);
+  // LDS read r (0..9) of the fragments of sub-step kk: A row block 0, the two
+  // halves of B column blocks 0..3, A row block 1 (the order the MFMAs use them)
+  auto rd = [&](const lds_u8_t* st_, int kk_, int r, bf16x8_t* na, bf16x8_t* nb) {
+    if (r == 0 || r == 9) {
+      const int i = r == 0 ? 0 : 1;
+      na[i] = lds_read_a(st_, swz(wm * 64 + i * 32 + lane % 32, kk_ * 2 + lane / 32));
+    } else {
+      const int jj = (r - 1) / 2, half = (r - 1) % 2;
+      const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_v4i16_t*)(st_ + b_off[jj][half] + kk_ * 16 * (BN * 2)));
+      __builtin_memcpy(reinterpret_cast<char*>(&nb[jj]) + 8 * half, &v, 8);
     }
   };
-
-  // Schedule of one k-step (one wave per SIMD, in-order issue). Stage t's
-  // loads are issued during step t - 2, spread over its four MFMA sub-steps,
-  // into the buffer that step t - 3 used (free since the barrier that ended
-  // step t - 3's reads). During sub-step kk the wave first issues the LDS
-  // reads of sub-step kk + 1 and its share of the loads, then the MFMAs of
-  // sub-step kk. Before the last sub-step's MFMAs it waits for the next stage,
-  // passes the barrier and reads the next stage's first fragments.
-  // sched_barrier keeps the compiler from regrouping these.
+  // Schedule of one k-step (one wave per SIMD, in-order issue: a wave issues
+  // at most one instruction per issue turn, so non-MFMA instructions placed
+  // between two MFMAs cost nothing while the matrix pipe is busy, and the same
+  // instructions issued as a block leave it idle). Stage t's loads go out
+  // during step t - 2 into the buffer that step t - 3 used (free since the
+  // barrier that ended step t - 3's reads). In sub-steps 0..2 each MFMA is
+  // followed by two of the ten LDS reads of the next sub-step's fragments (in
+  // the order its MFMAs use them) or by this step's loads (sub-step 2 also
+  // takes the last three). In sub-step 3 the wave runs two MFMAs, waits for
+  // the next stage and passes the barrier, then follows each further MFMA with
+  // two reads of the next stage's first fragments. sched_barrier pins this
+  // order.
   int issued = 0;
   for (; issued < nsteps && issued < kStages - 1; ++issued) issue_next();
   bf16x8_t fa[2][2], fb[2][4];
@@ -371,7 +364,8 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
     if (issued > 1) wait_vmcnt<kLoadsPerStage>();
     else wait_vmcnt<0>();
     stage_barrier();
-    read_frags(lds, 0, fa[0], fb[0]);
+#pragma unroll
+    for (int r = 0; r < 10; ++r) rd(lds, 0, r, fa[0], fb[0]);
   }
   int s = 0;  // global k-step being multiplied
   int cbuf = 0;
@@ -385,42 +379,70 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
       for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.f;
+    auto mm = [&](int c, int i, int jj) {
+      acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[c][jj], fa[c][i], acc[i][jj], 0, 0, 0);
+    };
 
     for (int kstep = 0; kstep < ksteps; ++kstep, ++s) {
       const lds_u8_t* st = lds + cbuf * kStageBytes;
       cbuf = (cbuf + 1 == kStages) ? 0 : cbuf + 1;
       const bool loads_now = issued < nsteps;  // stage s + 2 goes out during this step
+      const bool more = s + 1 < nsteps;
       if (loads_now) issue_begin();
+      // One MFMA, then up to two LDS reads or one load: the non-MFMA
+      // instructions of a sub-step issue in the shadows of its MFMAs.
 #pragma unroll
       for (int kk = 0; kk < BK / 16; ++kk) {
         const int cur = kk & 1;
         __builtin_amdgcn_sched_barrier(0);
         if (kk + 1 < BK / 16) {
-          read_frags(st, kk + 1, fa[cur ^ 1], fb[cur ^ 1]);
-          if (loads_now) issue_group(kk);
-          if (loads_now && kk + 2 == BK / 16) issue_group(kk + 1);
-        } else if (s + 1 < nsteps) {
-          // Stage s + 1 has landed once at most the vector-memory operations
-          // issued after its loads are in flight (the counter completes loads
-          // and stores in issue order): stage s + 2's loads, if issued, and
-          // the stores of an epilogue that ran right after step s - 1.
-          const bool next_loads = issued + (loads_now ? 1 : 0) > s + 2;
-          if (epi_step != s - 1) {
-            if (next_loads) wait_vmcnt<kLoadsPerStage>(); else wait_vmcnt<0>();
-          } else {
-            if (next_loads) wait_vmcnt<kLoadsPerStage + kStoresPerTile>();
-            else wait_vmcnt<kStoresPerTile>();
+          // reads of sub-step kk + 1 after MFMAs 0..4; this sub-step's loads
+          // after MFMAs 5..7 (sub-step 2 also takes the last three)
+#pragma unroll
+          for (int m = 0; m < 8; ++m) {
+            mm(cur, m / 4, m % 4);
+            __builtin_amdgcn_sched_barrier(0);
+            if (m < 5) {
+              rd(st, kk + 1, 2 * m, fa[cur ^ 1], fb[cur ^ 1]);
+              rd(st, kk + 1, 2 * m + 1, fa[cur ^ 1], fb[cur ^ 1]);
+            } else if (loads_now) {
+              load1(3 * kk + (m - 5));
+              if (kk == 2) load1(9 + (m - 5));
+            }
+            __builtin_amdgcn_sched_barrier(0);
           }
-          reads_done_barrier();  // everyone is done reading stage s; s + 1 is visible
-          read_frags(lds + cbuf * kStageBytes, 0, fa[cur ^ 1], fb[cur ^ 1]);
+        } else {
+          // two MFMAs, then the stage hand-over, then the reads of the next
+          // stage's first sub-step after MFMAs 2..6 (unconditional: after the
+          // last step they read a stage nobody uses)
+          mm(cur, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          mm(cur, 0, 1);
+          __builtin_amdgcn_sched_barrier(0);
+          wait_lds_reads();  // on every path: this wave is done reading stage s
+          if (more) {
+            const bool next_loads = issued + (loads_now ? 1 : 0) > s + 2;
+            if (epi_step != s - 1) {
+              if (next_loads) wait_vmcnt<kLoadsPerStage>(); else wait_vmcnt<0>();
+            } else {
+              if (next_loads) wait_vmcnt<kLoadsPerStage + kStoresPerTile>();
+              else wait_vmcnt<kStoresPerTile>();
+            }
+            stage_barrier();  // everyone is done reading stage s; s + 1 is visible
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          const lds_u8_t* nst = lds + cbuf * kStageBytes;
+#pragma unroll
+          for (int m = 2; m < 8; ++m) {
+            mm(cur, m / 4, m % 4);
+            __builtin_amdgcn_sched_barrier(0);
+            if (m < 7) {
+              rd(nst, 0, 2 * (m - 2), fa[cur ^ 1], fb[cur ^ 1]);
+              rd(nst, 0, 2 * (m - 2) + 1, fa[cur ^ 1], fb[cur ^ 1]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj)
-            acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[cur][jj], fa[cur][i],
-                                                                 acc[i][jj], 0, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
       if (loads_now) {

@@ -159,7 +159,7 @@ moe_status_t moe_rank_to_expert_reorder(const void* x_rank_major, const int32_t*
  *  y               bf16 [N_cap, H]   out
  * Errors: INVALID_ARG for E outside [1,1024], N_cap < 0 or > INT32_MAX,
  * H <= 0, I <= 0, NULL / misaligned pointers; UNSUPPORTED unless H % 64 == 0
- * and I % 64 == 0; WORKSPACE if too small. Offsets that break the stated
+ * and I % 64 == 0, and for H or I above 2^20; WORKSPACE if too small. Offsets that break the stated
  * contract are clamped on device to [0, N_cap] (no out-of-bounds access).
  * ------------------------------------------------------------------------ */
 moe_status_t moe_grouped_gemm_swiglu_workspace_size(int32_t E, int64_t N_cap, int32_t H,
@@ -193,7 +193,7 @@ moe_status_t moe_grouped_gemm_swiglu(const void* x, const int32_t* expert_offset
  *  workspace  moe_grouped_gemm_swiglu_grad_workspace_size bytes, 256-byte
  *             aligned (about 6 * N_cap * I bytes: dh and [dg | du])
  * Errors: as moe_grouped_gemm_swiglu (INVALID_ARG, UNSUPPORTED unless
- * H % 64 == 0 and I % 64 == 0, WORKSPACE).
+ * H % 64 == 0 and I % 64 == 0 or for H or I above 2^20, WORKSPACE).
  * ------------------------------------------------------------------------ */
 moe_status_t moe_grouped_gemm_swiglu_grad_workspace_size(int32_t E, int64_t N_cap, int32_t H,
                                                          int32_t I, size_t* bytes);

@@ -77,6 +77,17 @@ def test_workspace_sizes(lib):
     with pytest.raises(b.MoeError) as e:
         b.moe_grouped_gemm_swiglu_workspace_size(8, 100, 96, 64)
     assert e.value.status == UNSUPPORTED
+    # H and I above 2^20 (the epilogue's 32-bit tile offsets) are refused,
+    # for the forward and the backward alike
+    for H, I in ((1 << 20, 64), (64, 1 << 20)):
+        assert b.moe_grouped_gemm_swiglu_workspace_size(8, 100, H, I) > 0
+        assert b.moe_grouped_gemm_swiglu_grad_workspace_size(8, 100, H, I) > 0
+    for H, I in (((1 << 20) + 64, 64), (64, (1 << 20) + 64)):
+        for f in (b.moe_grouped_gemm_swiglu_workspace_size,
+                  b.moe_grouped_gemm_swiglu_grad_workspace_size):
+            with pytest.raises(b.MoeError) as e:
+                f(8, 100, H, I)
+            assert e.value.status == UNSUPPORTED
 
 
 P = 0x10000        # fake 16-byte aligned device address, never dereferenced
@@ -144,6 +155,8 @@ def test_gemm_checks(lib):
     assert _gemm(lib, H=0) == INVALID
     assert _gemm(lib, H=96) == UNSUPPORTED
     assert _gemm(lib, I=100) == UNSUPPORTED
+    assert _gemm(lib, H=(1 << 20) + 64) == UNSUPPORTED
+    assert _gemm(lib, I=(1 << 20) + 64) == UNSUPPORTED
     assert _gemm(lib, off=None) == INVALID
     assert _gemm(lib, wd=P + 4) == INVALID
     assert _gemm(lib, y=None) == INVALID

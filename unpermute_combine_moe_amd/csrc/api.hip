@@ -162,11 +162,16 @@ MOE_API moe_status_t moe_rank_to_expert_reorder(const void* x_rank_major, const 
 // --------------------------------------------------------------------------- grouped GEMM
 
 namespace {
+// Largest H and I: the GEMM epilogue addresses one 128-row output tile (at most
+// 128 x 2I or 128 x H bf16) with 32-bit byte offsets below 2^31.
+constexpr int32_t kMaxGemmDim = 1 << 20;
+
 moe_status_t check_gemm_sizes(int32_t E, int64_t N_cap, int32_t H, int32_t I) {
   if (E < 1 || E > MOE_MAX_EXPERTS) return MOE_ERR_INVALID_ARG;
   if (N_cap < 0 || N_cap > INT32_MAX) return MOE_ERR_INVALID_ARG;
   if (H <= 0 || I <= 0) return MOE_ERR_INVALID_ARG;
   if (H % 64 != 0 || I % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  if (H > kMaxGemmDim || I > kMaxGemmDim) return MOE_ERR_UNSUPPORTED;
   // the kernel indexes (row tile, column tile) pairs with 32-bit integers
   const int64_t max_row_tiles = N_cap / 128 + E + 1;
   const int64_t max_col_tiles = (std::max(H, I) + 127) / 128;
@@ -208,6 +213,7 @@ MOE_API moe_status_t moe_grouped_gemm_swiglu_grad_workspace_size(int32_t E, int6
   if (E < 1 || E > MOE_MAX_EXPERTS || N_cap < 0 || N_cap > INT32_MAX || H <= 0 || I <= 0)
     return MOE_ERR_INVALID_ARG;
   if (H % 64 != 0 || I % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  if (H > kMaxGemmDim || I > kMaxGemmDim) return MOE_ERR_UNSUPPORTED;
   *bytes = moe::gemm_grad_workspace_bytes(E, N_cap, H, I);
   return MOE_OK;
 }
@@ -220,6 +226,7 @@ MOE_API moe_status_t moe_grouped_gemm_swiglu_grad(
   if (E < 1 || E > MOE_MAX_EXPERTS || N_cap < 0 || N_cap > INT32_MAX || H <= 0 || I <= 0)
     return MOE_ERR_INVALID_ARG;
   if (H % 64 != 0 || I % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  if (H > kMaxGemmDim || I > kMaxGemmDim) return MOE_ERR_UNSUPPORTED;
   if (!word_ok(expert_offsets) || !row_ok(w_gate) || !row_ok(w_up) || !row_ok(w_down) ||
       !row_ok(dw_gate) || !row_ok(dw_up) || !row_ok(dw_down))
     return MOE_ERR_INVALID_ARG;

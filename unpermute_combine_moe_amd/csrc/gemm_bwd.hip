@@ -15,12 +15,17 @@
 //    e][n] (both row-contiguous): the contraction runs over the expert's rows,
 //    its ragged tail is zero-filled, and an expert without rows gets a zero
 //    tile. Tiles go out biggest expert first.
-// Operands are staged global -> registers -> LDS, double-buffered (the next
-// k-step's loads are in flight during this one's MFMAs). k-contiguous tiles sit
+// Operands are staged global -> registers -> LDS through two LDS buffers. In
+// k_bgemm_rows two register sets keep each k-step's loads in flight for a whole
+// step before they are stashed (measured 453 -> 422 us for dx on the skewed
+// layer); in k_bgemm_kgroup the next k-step's loads are in flight during this
+// one's MFMAs (the two-set form measured no faster there). k-contiguous tiles sit
 // in LDS as [row][k] with the XOR swizzle of the forward kernel and are read
 // with ds_read_b128; row-contiguous tiles sit as [k][col] and the MFMA operand
 // (8 consecutive k of one column per lane) is formed by ds_read_b64_tr_b16
 // transpose reads, as the forward kernel does for its weights.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -205,23 +210,26 @@ k_bgemm_rows(const uint16_t* __restrict__ A, int K, const uint16_t* __restrict__
     a_src[l] = A + int64_t(std::min(row0 + r, row_end - 1)) * K + kc * 8;
     b_row[l] = int64_t(e) * strideB + int64_t(std::min(n0 + r, Ncols - 1)) * ldb + kc * 8;
   }
-  uint4 ra[kLoads], rb[kLoads];
-  auto load = [&](int ks) {
+  // two register sets (see the k-loop below)
+  uint4 ra[2][kLoads], rb[2][kLoads];
+  auto load = [&](auto P, int ks) {
+    constexpr int p = decltype(P)::value;
     const int k0 = ks * TK;
     const uint16_t* bb = k0 < ksplit ? B0 : B1;
     const int kb = k0 < ksplit ? k0 : k0 - ksplit;
 #pragma unroll
     for (int l = 0; l < kLoads; ++l) {
-      ra[l] = *reinterpret_cast<const uint4*>(a_src[l] + k0);
-      rb[l] = *reinterpret_cast<const uint4*>(bb + b_row[l] + kb);
+      ra[p][l] = *reinterpret_cast<const uint4*>(a_src[l] + k0);
+      rb[p][l] = *reinterpret_cast<const uint4*>(bb + b_row[l] + kb);
     }
   };
-  auto stash = [&](int buf) {
+  auto stash = [&](auto P, int buf) {
+    constexpr int p = decltype(P)::value;
     lds_u8_t* st = lds + buf * kStageBytes;
 #pragma unroll
     for (int l = 0; l < kLoads; ++l) {
-      st_lds16(st, slot[l], ra[l]);
-      st_lds16(st + kTileBytes, slot[l], rb[l]);
+      st_lds16(st, slot[l], ra[p][l]);
+      st_lds16(st + kTileBytes, slot[l], rb[p][l]);
     }
   };
   f32x16_t acc[2][2];
@@ -232,13 +240,23 @@ k_bgemm_rows(const uint16_t* __restrict__ A, int K, const uint16_t* __restrict__
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   const int ksteps = K / TK;
-  load(0);
-  stash(0);
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  // k-step ks is multiplied from LDS buffer ks & 1; register set ks & 1 holds
+  // it between its load and its stash. A set is reloaded (two k-steps ahead)
+  // right after its stash, so its loads have a whole step to land. Stash and
+  // reload are unconditional (past the last k-step they repeat it, in bounds,
+  // and nothing reads the result), which keeps the compiler's vmcnt waits exact.
+  auto last = [&](int k) { return k < ksteps ? k : ksteps - 1; };
+  load(P0{}, 0);
+  load(P1{}, last(1));
+  stash(P0{}, 0);
+  load(P0{}, last(2));
   __syncthreads();
-  for (int ks = 0; ks < ksteps; ++ks) {
-    const int buf = ks & 1;
-    if (ks + 1 < ksteps) load(ks + 1);
-    const lds_u8_t* ta = lds + buf * kStageBytes;
+  auto step = [&](auto P, int ks) {
+    constexpr int p = decltype(P)::value;
+    using Q = std::integral_constant<int, 1 - p>;
+    const lds_u8_t* ta = lds + p * kStageBytes;
     const lds_u8_t* tb = ta + kTileBytes;
 #pragma unroll
     for (int kk = 0; kk < TK / 16; ++kk) {
@@ -253,9 +271,16 @@ k_bgemm_rows(const uint16_t* __restrict__ A, int K, const uint16_t* __restrict__
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
     }
-    if (ks + 1 < ksteps) stash(buf ^ 1);
+    stash(Q{}, 1 - p);       // k-step ks + 1
+    load(Q{}, last(ks + 3));
     __syncthreads();
+  };
+  int ks = 0;
+  for (; ks + 1 < ksteps; ks += 2) {
+    step(P0{}, ks);
+    step(P1{}, ks + 1);
   }
+  if (ks < ksteps) step(P0{}, ks);
   // the LDS is free: every wave has passed the k-loop's last barrier
   store_block(acc, lds + wave * 8192, row0 + wm * 64, row_end, n0 + wn * 64, Ncols, Ncols, C, C,
               Ncols, lane);

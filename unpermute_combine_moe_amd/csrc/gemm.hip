@@ -54,7 +54,6 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 constexpr int BM = 128;
 constexpr int BN = 256;  // B-columns per tile
 constexpr int BK = 64;
-constexpr int kThreads = 256;
 constexpr int kChunksA = BM * BK / 8;  // 16-byte chunks per stage
 constexpr int kChunksB = BN * BK / 8;
 constexpr int kSchedThreads = 1024;
@@ -104,10 +103,23 @@ typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
 
 constexpr int kStages = 3;
-constexpr int kLoadsA = kChunksA / kThreads;  // direct-to-LDS loads per thread per stage
-constexpr int kLoadsB = kChunksB / kThreads;
-constexpr int kLoadsPerStage = kLoadsA + kLoadsB;
 constexpr int kStageBytes = (kChunksA + kChunksB) * 16;
+
+// Waves of a workgroup: 2 (64-row halves) x kWavesN (B-column blocks). The
+// gate/up passes use 4 waves (one per SIMD, 64 x 128 each); the down pass,
+// whose tiles are only 8 k-steps long, uses 8 (two per SIMD, 64 x 64 each),
+// measured faster there (217 against 227 us) and not for gate/up.
+template <int kMode>
+struct Layout {
+  static constexpr int kWavesN = (kMode == 1) ? 4 : 2;
+  static constexpr int kThreads = 2 * kWavesN * kWave;
+  static constexpr int kColFrags = BN / 32 / kWavesN;     // 32-column MFMA blocks per wave
+  static constexpr int kLoadsA = kChunksA / kThreads;     // direct-to-LDS loads per thread per stage
+  static constexpr int kLoadsB = kChunksB / kThreads;
+  static constexpr int kLoadsPerStage = kLoadsA + kLoadsB;
+  static constexpr int kReads = 2 + 2 * kColFrags;        // LDS fragment reads per sub-step
+  static constexpr int kMfmas = 2 * kColFrags;            // MFMAs per sub-step
+};
 // Epilogue. Each 32-row fragment of a wave's output goes through LDS: the
 // lanes write their MFMA results (one token row per lane, four consecutive
 // columns per register group) as packed bf16, then read the fragment back
@@ -119,8 +131,9 @@ constexpr int kStageBytes = (kChunksA + kChunksB) * 16;
 // conflicts. kStores counts the vector-memory stores a wave issues per tile.
 template <int kMode>
 struct EpiloguePlan {
-  static constexpr int kOutFrags = (kMode == 1) ? 4 : 2;
-  static constexpr int kRowBytes = (kMode == 0) ? 128 : 256;
+  static constexpr int kOutFrags =
+      (kMode == 1) ? Layout<kMode>::kColFrags : Layout<kMode>::kColFrags / 2;
+  static constexpr int kRowBytes = kOutFrags * 64 * (kMode == 2 ? 2 : 1);
   static constexpr int kChunks = kRowBytes / 16;        // per staged row
   static constexpr int kRowsPerStore = kWave / kChunks;  // rows one wave-wide store covers
   static constexpr int kStoresPerFrag = 32 / kRowsPerStore;
@@ -133,6 +146,7 @@ __device__ __forceinline__ int stage_chunk(int row, int chunk) {
   // rows of 256 B start on the same bank: key = row % 16; rows of 128 B
   // alternate between the two bank halves: key = (row / 2) % 8
   return kRowBytes == 256 ? (chunk ^ (row & 15)) : (chunk ^ ((row >> 1) & 7));
+  static_assert(kRowBytes == 256 || kRowBytes == 128, "staged row sizes");
 }
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
@@ -179,7 +193,7 @@ __device__ __forceinline__ bf16x8_t lds_read_a(const lds_u8_t* base, int slot) {
 // epilogue writes C [N, 2 * Ncols] = [dg | du], dg = dh * u * s (1 + g (1 - s)),
 // du = dh * g * s, s = 1 / (1 + exp(-g)) (the SwiGLU derivative).
 template <int kMode>
-__global__ void __launch_bounds__(kThreads, 1)
+__global__ void __launch_bounds__(Layout<kMode>::kThreads, 1)
 k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0,
        const uint16_t* __restrict__ B1, int Ncols, const int32_t* __restrict__ ws, int E,
        uint16_t* __restrict__ C, const uint16_t* __restrict__ aux) {
@@ -189,7 +203,8 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
   __shared__ int32_t s_prefix[kMaxExperts + 1];
   __shared__ int32_t s_offs[kMaxExperts + 1];
   lds_u8_t* lds = (lds_u8_t*)(smem);
-  for (int i = threadIdx.x; i <= E; i += kThreads) {
+  using L = Layout<kMode>;
+  for (int i = threadIdx.x; i <= E; i += L::kThreads) {
     s_prefix[i] = ws[i];
     s_offs[i] = ws[E + 1 + i];
   }
@@ -200,11 +215,11 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
   const int lane = tid % kWave;
   const int wave = tid / kWave;
   const int wm = wave & 1;   // 64-row half of the tile
-  const int wn = wave >> 1;  // B-column half
+  const int wn = wave >> 1;  // B-column block
 
   constexpr int kOutCols = (kMode == 1) ? BN : BN / 2;
   constexpr int kStoresPerTile = EpiloguePlan<kMode>::kStores;
-  static_assert(kLoadsPerStage + kStoresPerTile < 64, "vmcnt field is 6 bits");
+  static_assert(L::kLoadsPerStage + kStoresPerTile < 64, "vmcnt field is 6 bits");
   const int col_tiles = (Ncols + kOutCols - 1) / kOutCols;
   const int row_tiles = prefix[E];
   const int total = row_tiles * col_tiles;  // < 2^31: at most (2^31 / 128 + 1024) * 32
@@ -219,13 +234,16 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
 
   // LDS byte offsets (within a stage) of this lane's B-operand transpose reads
   // for sub-step 0; sub-step kk adds 16 rows, which keeps k & 3 and the swizzle
-  int b_off[4][2];  // [n-frag][half]
+  int b_off[L::kColFrags][2];  // [n-frag][half]
   const int g16 = lane / 16, i16 = lane % 16;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < L::kColFrags; ++j) {
+    // gate/up: the first half of the blocks are gate columns, the second the
+    // matching up columns
+    constexpr int kHalf = L::kColFrags / 2;
     int ncol;
-    if (kMode != 1) ncol = (j < 2 ? 0 : BN / 2) + wn * 64 + (j % 2) * 32;
-    else ncol = wn * 128 + j * 32;
+    if (kMode != 1) ncol = (j < kHalf ? 0 : BN / 2) + wn * (BN / 2 / L::kWavesN) + (j % kHalf) * 32;
+    else ncol = wn * (BN / L::kWavesN) + j * 32;
     const int n = ncol + 16 * (g16 % 2) + 4 * (i16 % 4);
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -275,21 +293,21 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
   int lj = 0;
   int lk = 0;
   int lbuf = 0;
-  const uint16_t* a_src[kLoadsA];
-  const uint16_t* b_src[kLoadsB];
+  const uint16_t* a_src[L::kLoadsA];
+  const uint16_t* b_src[L::kLoadsB];
   auto load_tile_sources = [&](int j) {
     const TileInfo t = tile_info(j);
 #pragma unroll
-    for (int i = 0; i < kLoadsA; ++i) {
-      const int slot = i * kThreads + wave * kWave + lane;
+    for (int i = 0; i < L::kLoadsA; ++i) {
+      const int slot = i * L::kThreads + wave * kWave + lane;
       const int m = slot >> 3;
       const int kc = (slot & 7) ^ ((m >> 1) & 7);
       const int r = std::min(t.row0 + m, t.row_end - 1);
       a_src[i] = A + int64_t(r) * Kdim + kc * 8;
     }
 #pragma unroll
-    for (int i = 0; i < kLoadsB; ++i) {
-      const int slot = i * kThreads + wave * kWave + lane;
+    for (int i = 0; i < L::kLoadsB; ++i) {
+      const int slot = i * L::kThreads + wave * kWave + lane;
       const int k = slot >> 5;
       const int c = (slot & 31) ^ (4 * (k & 3));
       const uint16_t* base;
@@ -312,11 +330,11 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
   };
   // load i (0 .. kLoadsPerStage - 1) of the stage being issued
   auto load1 = [&](int i) {
-    if (i < kLoadsA)
-      load_lds16(a_src[i] + lk * BK, l_st + i * kThreads * 16);
+    if (i < L::kLoadsA)
+      load_lds16(a_src[i] + lk * BK, l_st + i * L::kThreads * 16);
     else
-      load_lds16(b_src[i - kLoadsA] + int64_t(lk) * BK * Ncols,
-                 l_st + (kChunksA + (i - kLoadsA) * kThreads) * 16);
+      load_lds16(b_src[i - L::kLoadsA] + int64_t(lk) * BK * Ncols,
+                 l_st + (kChunksA + (i - L::kLoadsA) * L::kThreads) * 16);
   };
   auto issue_end = [&]() {
     lbuf = (lbuf + 1 == kStages) ? 0 : lbuf + 1;
@@ -328,14 +346,15 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
   auto issue_next = [&]() {
     issue_begin();
 #pragma unroll
-    for (int i = 0; i < kLoadsPerStage; ++i) load1(i);
+    for (int i = 0; i < L::kLoadsPerStage; ++i) load1(i);
     issue_end();
   };
 
-  // LDS read r (0..9) of the fragments of sub-step kk: A row block 0, the two
-  // halves of B column blocks 0..3, A row block 1 (the order the MFMAs use them)
+  // LDS read r (0 .. kReads - 1) of the fragments of sub-step kk: A row block
+  // 0, the two halves of each B column block, A row block 1 (the order the
+  // MFMAs use them)
   auto rd = [&](const lds_u8_t* st_, int kk_, int r, bf16x8_t* na, bf16x8_t* nb) {
-    if (r == 0 || r == 9) {
+    if (r == 0 || r == L::kReads - 1) {
       const int i = r == 0 ? 0 : 1;
       na[i] = lds_read_a(st_, swz(wm * 64 + i * 32 + lane % 32, kk_ * 2 + lane / 32));
     } else {
@@ -359,24 +378,24 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
   // order.
   int issued = 0;
   for (; issued < nsteps && issued < kStages - 1; ++issued) issue_next();
-  bf16x8_t fa[2][2], fb[2][4];
+  bf16x8_t fa[2][2], fb[2][L::kColFrags];
   if (nsteps > 0) {
-    if (issued > 1) wait_vmcnt<kLoadsPerStage>();
+    if (issued > 1) wait_vmcnt<L::kLoadsPerStage>();
     else wait_vmcnt<0>();
     stage_barrier();
 #pragma unroll
-    for (int r = 0; r < 10; ++r) rd(lds, 0, r, fa[0], fb[0]);
+    for (int r = 0; r < L::kReads; ++r) rd(lds, 0, r, fa[0], fb[0]);
   }
   int s = 0;  // global k-step being multiplied
   int cbuf = 0;
   int epi_step = -8;  // k-step after which the last epilogue ran
   for (int j = 0; j < ntiles; ++j) {
     const TileInfo ci = tile_info(j);
-    f32x16_t acc[2][4];
+    f32x16_t acc[2][L::kColFrags];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj)
+      for (int jj = 0; jj < L::kColFrags; ++jj)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][jj][r] = 0.f;
     auto mm = [&](int c, int i, int jj) {
@@ -399,15 +418,20 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
           // reads of sub-step kk + 1 after MFMAs 0..4; this sub-step's loads
           // after MFMAs 5..7 (sub-step 2 also takes the last three)
 #pragma unroll
-          for (int m = 0; m < 8; ++m) {
-            mm(cur, m / 4, m % 4);
+          for (int m = 0; m < L::kMfmas; ++m) {
+            mm(cur, m / L::kColFrags, m % L::kColFrags);
             __builtin_amdgcn_sched_barrier(0);
-            if (m < 5) {
+            if (m < L::kReads / 2) {
               rd(st, kk + 1, 2 * m, fa[cur ^ 1], fb[cur ^ 1]);
               rd(st, kk + 1, 2 * m + 1, fa[cur ^ 1], fb[cur ^ 1]);
             } else if (loads_now) {
-              load1(3 * kk + (m - 5));
-              if (kk == 2) load1(9 + (m - 5));
+              if (L::kWavesN == 2) {  // 12 loads: 3 in sub-steps 0 and 1, 6 in 2
+                load1(3 * kk + (m - 5));
+                if (kk == 2) load1(9 + (m - 5));
+              } else {                // 6 loads: 2 per sub-step
+                load1(2 * kk);
+                load1(2 * kk + 1);
+              }
             }
             __builtin_amdgcn_sched_barrier(0);
           }
@@ -423,23 +447,25 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
           if (more) {
             const bool next_loads = issued + (loads_now ? 1 : 0) > s + 2;
             if (epi_step != s - 1) {
-              if (next_loads) wait_vmcnt<kLoadsPerStage>(); else wait_vmcnt<0>();
+              if (next_loads) wait_vmcnt<L::kLoadsPerStage>(); else wait_vmcnt<0>();
             } else {
-              if (next_loads) wait_vmcnt<kLoadsPerStage + kStoresPerTile>();
+              if (next_loads) wait_vmcnt<L::kLoadsPerStage + kStoresPerTile>();
               else wait_vmcnt<kStoresPerTile>();
             }
             stage_barrier();  // everyone is done reading stage s; s + 1 is visible
           }
           __builtin_amdgcn_sched_barrier(0);
           const lds_u8_t* nst = lds + cbuf * kStageBytes;
+          // reads per remaining MFMA: 2 (4 waves: 10 reads over 6 MFMAs) or
+          // 3 (8 waves: 6 reads over 2 MFMAs)
+          constexpr int kRpm = (L::kReads + L::kMfmas - 3) / (L::kMfmas - 2);
 #pragma unroll
-          for (int m = 2; m < 8; ++m) {
-            mm(cur, m / 4, m % 4);
+          for (int m = 2; m < L::kMfmas; ++m) {
+            mm(cur, m / L::kColFrags, m % L::kColFrags);
             __builtin_amdgcn_sched_barrier(0);
-            if (m < 7) {
-              rd(nst, 0, 2 * (m - 2), fa[cur ^ 1], fb[cur ^ 1]);
-              rd(nst, 0, 2 * (m - 2) + 1, fa[cur ^ 1], fb[cur ^ 1]);
-            }
+#pragma unroll
+            for (int r = (m - 2) * kRpm; r < (m - 1) * kRpm && r < L::kReads; ++r)
+              rd(nst, 0, r, fa[cur ^ 1], fb[cur ^ 1]);
             __builtin_amdgcn_sched_barrier(0);
           }
         }
@@ -467,7 +493,7 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
       const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
           C + int64_t(ci.row0) * Ncols * ldc, 0, (ci.row_end - ci.row0) * Ncols * ldc * 2,
           0x00020000);
-      const int wcol0 = ci.n0 + ((kMode == 1) ? wn * 128 : wn * 64);  // wave's first output column
+      const int wcol0 = ci.n0 + ((kMode == 1) ? wn * (BN / L::kWavesN) : wn * (BN / 2 / L::kWavesN));  // wave's first output column
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int r = lane % 32;  // this lane's row in the fragment
@@ -490,11 +516,11 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
             for (int k = 0; k < 4; ++k) {
               if (kMode == 0) {
                 const float g = acc[i][jj][4 * q + k];
-                const float u = acc[i][jj + 2][4 * q + k];
+                const float u = acc[i][jj + EP::kOutFrags][4 * q + k];
                 v[k] = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
               } else if (kMode == 2) {
                 const float g = acc[i][jj][4 * q + k];
-                const float u = acc[i][jj + 2][4 * q + k];
+                const float u = acc[i][jj + EP::kOutFrags][4 * q + k];
                 const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g));
                 v[k] = d[k] * u * sg * (1.0f + g * (1.0f - sg));  // dg
                 w[k] = d[k] * g * sg;                              // du
@@ -511,7 +537,7 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
             if (kMode == 2) {  // du in the second half of the staged row
               const u32x2_t pw = {pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3])};
               *reinterpret_cast<__attribute__((address_space(3))) u32x2_t*>(
-                  stg + r * EP::kRowBytes + stage_chunk<EP::kRowBytes>(r, 8 + chunk) * 16 +
+                  stg + r * EP::kRowBytes + stage_chunk<EP::kRowBytes>(r, EP::kChunks / 2 + chunk) * 16 +
                   (lane / 32) * 8) = pw;
             }
           }
@@ -528,8 +554,8 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
           const int lrow = wm * 64 + i * 32 + rr;  // row within the tile
           int col, dst_col;
           if (kMode == 2) {
-            col = wcol0 + (c % 8) * 8;
-            dst_col = (c < 8) ? col : Ncols + col;
+            col = wcol0 + (c % (EP::kChunks / 2)) * 8;
+            dst_col = (c < EP::kChunks / 2) ? col : Ncols + col;
           } else {
             col = wcol0 + c * 8;
             dst_col = col;
@@ -575,8 +601,10 @@ hipError_t launch_grouped_gemm_swiglu(const uint16_t* x, const int32_t* offsets,
   hipLaunchKernelGGL(k_gemm_sched, dim3(1), dim3(kSchedThreads), 0, st, offsets, E, N_cap, w);
   if (N_cap == 0) return hipGetLastError();
   const int G = persistent_grid();
-  hipLaunchKernelGGL(k_gemm<0>, dim3(G), dim3(kThreads), 0, st, x, H, wg, wu, I, w, E, h, nullptr);
-  hipLaunchKernelGGL(k_gemm<1>, dim3(G), dim3(kThreads), 0, st, h, I, wd, nullptr, H, w, E, y,
+  hipLaunchKernelGGL(k_gemm<0>, dim3(G), dim3(Layout<0>::kThreads), 0, st, x, H, wg, wu, I, w, E,
+                     h, nullptr);
+  hipLaunchKernelGGL(k_gemm<1>, dim3(G), dim3(Layout<1>::kThreads), 0, st, h, I, wd, nullptr, H, w,
+                     E, y,
                      nullptr);
   return hipGetLastError();
 }
@@ -631,7 +659,8 @@ hipError_t launch_grouped_gemm_swiglu_grad(const uint16_t* x, const int32_t* off
     if (err != hipSuccess) return err;
     // [dg | du] from the recomputed gate and up tiles
     const int G = persistent_grid();
-    hipLaunchKernelGGL(k_gemm<2>, dim3(G), dim3(kThreads), 0, st, x, H, wg, wu, I, w, E, dgu, dh);
+    hipLaunchKernelGGL(k_gemm<2>, dim3(G), dim3(Layout<2>::kThreads), 0, st, x, H, wg, wu, I, w, E,
+                       dgu, dh);
     // dx = [dg | du] [Wg ; Wu]^T: B_e = Wg[e], Wu[e] as [H][I] side by side along k
     err = launch_bgemm_rows(dgu, 2 * I, wg, wu, I, I, int64_t(H) * I, H, N_cap, bt, E, dx, st);
     if (err != hipSuccess) return err;

@@ -29,18 +29,27 @@ struct PermutePlan {
   int64_t nblk; // number of chunks
 };
 
+// Threads that share one expert's walk of the count table: a power of two,
+// at most a wave, with threads-per-expert x E within the workgroup.
+__host__ __device__ inline int walk_threads(int E) {
+  int t = 1;
+  while (t < kWave && 2 * t * E <= kChunkThreads) t *= 2;
+  return t;
+}
+
 // Chunks are sized so the (chunk, expert) count table holds at most
 // kTableMax entries (every scatter workgroup reads all of it), with at least
-// kMinIters slots per lane: more, smaller chunks lengthen the table walk more
-// than they shorten the scatter.
+// 8 / walk_threads(E) (and at least 2) slots per lane: more, smaller chunks
+// lengthen the table walk, which walk_threads(E) threads per expert share,
+// and shorten the counting and the scatter.
 constexpr int64_t kTableMax = 16384;
-constexpr int kMinIters = 8;
 
 PermutePlan plan_for(int64_t S, int E) {
   PermutePlan p;
   const int64_t target = std::max<int64_t>(1, std::min<int64_t>(256, kTableMax / E));
+  const int min_iters = std::max(2, 8 / walk_threads(E));
   p.iters = static_cast<int>(
-      std::max<int64_t>(kMinIters, ceil_div(S, int64_t(kChunkThreads) * target)));
+      std::max<int64_t>(min_iters, ceil_div(S, int64_t(kChunkThreads) * target)));
   p.chunk = int64_t(kChunkThreads) * p.iters;
   p.nblk = ceil_div(S, p.chunk);
   return p;
@@ -181,20 +190,33 @@ k_route_scan_scatter(const int32_t* __restrict__ ids, SlotMask mk, int64_t S, in
   int32_t* off = before + E;
   int32_t* part = off + E;
   const int64_t b = blockIdx.x;
-  for (int e = threadIdx.x; e < E; e += kChunkThreads) {
+  // tpe consecutive threads (an aligned group inside one wave) share expert
+  // e's walk, each taking every tpe-th chunk; their sums meet by xor shuffles
+  const int tpe = walk_threads(E);
+  for (int g = threadIdx.x; g < E * tpe; g += kChunkThreads) {
+    const int e = g / tpe, sub = g % tpe;
     int32_t tot = 0, pre = 0;
-    for (int64_t b0 = 0; b0 < nblk; b0 += kBatch) {
+    for (int64_t b0 = sub; b0 < nblk; b0 += int64_t(kBatch) * tpe) {
       int32_t c[kBatch];
 #pragma unroll
-      for (int q = 0; q < kBatch; ++q) c[q] = (b0 + q < nblk) ? hist[(b0 + q) * E + e] : 0;
+      for (int q = 0; q < kBatch; ++q) {
+        const int64_t bq = b0 + int64_t(q) * tpe;
+        c[q] = (bq < nblk) ? hist[bq * E + e] : 0;
+      }
 #pragma unroll
       for (int q = 0; q < kBatch; ++q) {
         tot += c[q];
-        pre += (b0 + q < b) ? c[q] : 0;
+        pre += (b0 + int64_t(q) * tpe < b) ? c[q] : 0;
       }
     }
-    off[e] = tot;
-    before[e] = pre;
+    for (int o = tpe / 2; o > 0; o >>= 1) {
+      tot += __shfl_xor(tot, o, kWave);
+      pre += __shfl_xor(pre, o, kWave);
+    }
+    if (sub == 0) {
+      off[e] = tot;
+      before[e] = pre;
+    }
   }
   __syncthreads();
   // exclusive scan of the expert totals: each thread a contiguous run of experts

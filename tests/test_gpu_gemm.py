@@ -50,6 +50,35 @@ def test_gemm_small(moe_lib, counts, H, I, seed):
     assert_h_within_ulp(hb[:n], h_ref)
 
 
+def _many_expert_counts(seed, E=1000, busy=40):
+    """E experts, most of them empty; `busy` of them (the last one included)
+    with 1..300 rows."""
+    rng = np.random.default_rng(seed)
+    counts = np.zeros(E, np.int64)
+    sel = np.concatenate([rng.choice(E - 1, busy - 1, replace=False), [E - 1]])
+    counts[sel] = rng.integers(1, 301, size=busy)
+    return counts
+
+
+def test_gemm_many_experts(moe_lib):
+    # E = 1000 (not a multiple of 16): the tile lookup's last expert block is
+    # partial, and most experts have no rows
+    counts = _many_expert_counts(31)
+    rng = np.random.default_rng(32)
+    E, H, I = len(counts), 64, 64
+    off = _offsets(counts)
+    N = int(off[-1]) + 5
+    x = W.normal_bf16(rng, (N, H))
+    wg = W.normal_bf16(rng, (E, H, I), 0.02)
+    wu = W.normal_bf16(rng, (E, H, I), 0.02)
+    wd = W.normal_bf16(rng, (E, I, H), 0.02)
+    hb, yb = _gemm(moe_lib, x, off, wg, wu, wd)
+    n = int(off[-1])
+    h_ref, y_ref = oracle.grouped_swiglu(x[:n], off, wg, wu, wd)
+    assert np.max(np.abs(f64(yb[:n]) - y_ref)) <= gemm_tol(H)
+    assert_h_within_ulp(hb[:n], h_ref)
+
+
 def test_gemm_config1(moe_lib):
     g = W.gen_c1()
     c = g["cfg"]

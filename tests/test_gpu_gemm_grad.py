@@ -89,6 +89,22 @@ def test_gemm_grad_small(moe_lib, counts, H, I, seed):
             assert not got["dw_gate"][e].any() and not got["dw_down"][e].any()
 
 
+def test_gemm_grad_many_experts(moe_lib):
+    # E = 1000, most experts empty (their weight gradients must be zero)
+    rng = np.random.default_rng(41)
+    E = 1000
+    counts = np.zeros(E, np.int64)
+    sel = np.concatenate([rng.choice(E - 1, 29, replace=False), [E - 1]])
+    counts[sel] = rng.integers(1, 201, size=30)
+    x, off, wg, wu, wd, dy = _data(42, counts, 64, 64)
+    got = _gpu(moe_lib, x, off, wg, wu, wd, dy)
+    ref = oracle.grouped_swiglu_grad(x, off, wg, wu, wd, dy)
+    _check(got, ref, x, off, wg, wu, wd, dy)
+    empty = counts == 0
+    assert not got["dw_gate"][empty].any() and not got["dw_up"][empty].any()
+    assert not got["dw_down"][empty].any()
+
+
 def test_gemm_grad_config1(moe_lib):
     g = W.gen_c1()
     c = g["cfg"]

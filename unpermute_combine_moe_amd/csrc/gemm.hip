@@ -453,6 +453,10 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
               else wait_vmcnt<kStoresPerTile>();
             }
             stage_barrier();  // everyone is done reading stage s; s + 1 is visible
+          } else {
+            // the workgroup's last k-step: the epilogue stages its output in
+            // stage s, so every wave must be done reading it first
+            stage_barrier();
           }
           __builtin_amdgcn_sched_barrier(0);
           const lds_u8_t* nst = lds + cbuf * kStageBytes;
@@ -482,9 +486,10 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
       using EP = EpiloguePlan<kMode>;
       static_assert(4 * EP::kWaveBytes <= kStageBytes, "staging fits one ring stage");
       // Staging space: the ring stage of step s - 1, which every wave has
-      // finished reading (the barrier of that step's last sub-step) and which
-      // is refilled only by stage s + 2's loads, issued during step s after
-      // the barrier at the end of this epilogue.
+      // finished reading (the barrier of that step's last sub-step, taken on
+      // the workgroup's last step too) and which is refilled only by stage
+      // s + 2's loads, issued during step s after the barrier at the end of
+      // this epilogue.
       lds_u8_t* stg = lds + ((cbuf + kStages - 1) % kStages) * kStageBytes + wave * EP::kWaveBytes;
       constexpr int ldc = (kMode == 2) ? 2 : 1;  // C row stride in units of Ncols
       // Buffer stores: a store whose offset lies past the tile's last valid

@@ -90,3 +90,26 @@ def assert_dot_bound(got, ref, terms, what="", term_units=4, out_units=2):
     assert not bad.any(), (f"{what}: {int(bad.sum())} of {ref.size} elements outside the bf16 "
                            f"dot-product bound; worst err/bound {float(np.max(err / (bound + 1e-300))):.3f}")
     return float(np.max(err / (bound + 1e-300))) if ref.size else 0.0
+
+
+def ffn_grad_worst(got, ref, x, off, wg, wu, wd, dy, h64, experts):
+    """Checks the grouped SwiGLU FFN backward of the given experts against the
+    oracle's fp64 result with assert_dot_bound: dx rows of each expert and its
+    three weight gradients. The magnitudes of the exact terms come from the
+    oracle's intermediates (|dg|, |du|, the forward's fp64 h). Returns the worst
+    err/bound ratio per output."""
+    f = lambda b: np.abs(f64(b))
+    worst = dict(dx=0.0, dw_gate=0.0, dw_up=0.0, dw_down=0.0)
+    for e in experts:
+        lo, hi = int(off[e]), int(off[e + 1])
+        dg, du = np.abs(ref["dg"][lo:hi]), np.abs(ref["du"][lo:hi])
+        X = f(x[lo:hi])
+        pairs = (("dx", got["dx"][lo:hi], ref["dx"][lo:hi],
+                  lambda: dg @ f(wg[e]).T + du @ f(wu[e]).T),
+                 ("dw_gate", got["dw_gate"][e], ref["dwg"][e], lambda: X.T @ dg),
+                 ("dw_up", got["dw_up"][e], ref["dwu"][e], lambda: X.T @ du),
+                 ("dw_down", got["dw_down"][e], ref["dwd"][e],
+                  lambda: np.abs(h64[lo:hi]).T @ f(dy[lo:hi])))
+        for name, g, r, terms in pairs:
+            worst[name] = max(worst[name], assert_dot_bound(g, r, terms(), f"{name} expert {e}"))
+    return worst

@@ -23,9 +23,18 @@ def _run(moe, g, perm, ros, probs):
     assert_rel(dpr.cpu().numpy(), rdpr64, 1e-2, "d_probs")
 
 
+# Kernel instance reached (16-byte chunks per lane, waves per token): rows of
+# at least 2048 elements below 32,768 tokens take two waves per token.
 @pytest.mark.parametrize("T,K,E,H,seed", [
-    (1, 1, 1, 8, 0), (300, 2, 8, 128, 1), (1000, 6, 64, 264, 2), (513, 8, 32, 4096, 3),
-    (64, 16, 20, 8200, 4),  # H past the register-resident path
+    (1, 1, 1, 8, 0), (300, 2, 8, 128, 1), (1000, 6, 64, 264, 2),   # 1 chunk, 1 wave
+    (300, 2, 8, 1000, 6),          # 2 chunks, 1 wave
+    (257, 4, 16, 1536, 7),         # 4 chunks, 1 wave (3 used)
+    (8192, 2, 64, 2048, 11),       # 2 chunks, 2 waves (the skewed layer's shape)
+    (513, 8, 32, 4096, 3),         # 4 chunks, 2 waves
+    (200, 3, 16, 6144, 8),         # 8 chunks, 2 waves (6 used)
+    (32768, 1, 4, 2056, 9),        # 8 chunks, 1 wave (5 used)
+    (32768, 1, 4, 4104, 10),       # 16 chunks, 1 wave (9 used)
+    (64, 16, 20, 8200, 4),         # 16 chunks, 2 waves (9 used)
 ])
 def test_grad_random(moe_lib, T, K, E, H, seed):
     rng = np.random.default_rng(seed)

@@ -26,7 +26,9 @@
  *    matching *_workspace_size call returns; their contents are undefined
  *    afterwards. Calls that share one workspace on one stream are fine; calls
  *    that overlap in time must use different workspaces.
- *  - The library holds no global state: calls are re-entrant.
+ *  - The library holds no global state, and calls are re-entrant, with one
+ *    exception: moe_permute_noalloc keeps its count table in a device array
+ *    that the library owns (one per GPU, 64 KiB).
  *
  * Source passages (page title, then section):
  *  [EP]  "Coverage for hyper_parallel/core/expert_parallel/expert_parallel.py"
@@ -106,6 +108,27 @@ moe_status_t moe_permute(const void* x, const int32_t* expert_ids, const uint8_t
                          int32_t num_experts, void* permuted, int32_t* sorted_slot,
                          int32_t* row_of_slot, int32_t* expert_counts, int32_t* expert_offsets,
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * moe_permute_noalloc -- moe_permute without a workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Same arguments, outputs and checks as moe_permute, minus the workspace. The
+ * count table lives in a 64 KiB device array of the library, one per GPU,
+ * kept until the process ends; the call allocates nothing. Every table size
+ * the permute's planner makes fits (at most 16,384 int32 entries); a larger
+ * one would be refused with MOE_ERR_WORKSPACE. The first call on a GPU looks
+ * up that GPU's array (MOE_ERR_HIP if the lookup fails). Calls on one GPU
+ * share its array: calls on the same stream are fine, calls that overlap in
+ * time on different streams of one GPU race and must not be issued.
+ * ------------------------------------------------------------------------ */
+moe_status_t moe_permute_noalloc(const void* x, const int32_t* expert_ids,
+                                 const uint8_t* active_mask, int32_t mask_per_slot, int64_t T,
+                                 int32_t H, int32_t K, int32_t num_experts, void* permuted,
+                                 int32_t* sorted_slot, int32_t* row_of_slot,
+                                 int32_t* expert_counts, int32_t* expert_offsets,
+                                 hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * moe_rank_to_expert_reorder -- receive buffer, rank-major -> expert-major.

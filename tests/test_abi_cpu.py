@@ -120,6 +120,32 @@ def test_permute_checks(lib):
     assert _permute(lib, mask=P, per_slot=2) == INVALID
 
 
+def test_permute_table_fits_the_noalloc_array(lib):
+    """moe_permute_noalloc keeps the permute's count table in a 64 KiB array:
+    every legal (T*K, E) must need at most that."""
+    from unpermute_combine_moe_amd import binding as b
+
+    Es = sorted({1, 2, 3, 5, 7, 8, 63, 64, 65, 100, 127, 128, 255, 256, 257, 500, 511, 512, 513,
+                 1000, 1023, 1024})
+    Ss = sorted({0, 1, 2, 255, 256, 257, 511, 512, 513, 4095, 4096, 24576, 65536, 65537, 131072,
+                 10**6, 2**24 + 3, 2**28, 2**31 - 1})
+    worst = max(b.moe_permute_workspace_size(S, 1, E) for S in Ss for E in Es)
+    assert worst <= 64 * 1024
+
+
+@no_gpu
+def test_permute_noalloc_checks(lib):
+    # size checks come first, before any device lookup
+    f = lambda T=16, K=2, E=4: lib.moe_permute_noalloc(P, P, None, 0, T, 64, K, E, P, P, P, P, P,
+                                                       None)
+    assert f(T=-1) == INVALID
+    assert f(K=0) == INVALID
+    assert f(K=17) == INVALID
+    assert f(E=0) == INVALID
+    assert f(E=1025) == INVALID
+    assert f(T=2**30, K=4) == INVALID
+
+
 def _reorder(lib, x=P, cnt=P, R=8, El=32, N=1000, H=64, y=P, perm=P, inv=P, tpe=P, off=P, ws=P,
              wsb=1 << 20):
     return lib.moe_rank_to_expert_reorder(x, cnt, R, El, N, H, y, perm, inv, tpe, off, ws, wsb,

@@ -43,7 +43,7 @@ class MoeSpecialExperts(ctypes.Structure):
 
 EXPORTS = (
     "moe_status_str", "moe_abi_version",
-    "moe_permute_workspace_size", "moe_permute",
+    "moe_permute_workspace_size", "moe_permute", "moe_permute_noalloc",
     "moe_rank_to_expert_reorder_workspace_size", "moe_rank_to_expert_reorder",
     "moe_grouped_gemm_swiglu_workspace_size", "moe_grouped_gemm_swiglu",
     "moe_unpermute_combine", "moe_unpermute_grad", "moe_permute_grad",
@@ -73,6 +73,8 @@ def load(path: str = LIB_PATH):
     lib.moe_permute_workspace_size.argtypes = [_i64, _i32, _i32, sz]
     lib.moe_permute.argtypes = [_vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
                                 _vp, _vp, ctypes.c_size_t, _vp]
+    lib.moe_permute_noalloc.argtypes = [_vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _vp, _vp,
+                                        _vp, _vp, _vp, _vp]
     lib.moe_rank_to_expert_reorder_workspace_size.argtypes = [_i32, _i32, sz]
     lib.moe_rank_to_expert_reorder.argtypes = [_vp, _vp, _i32, _i32, _i64, _i32, _vp, _vp, _vp,
                                                _vp, _vp, _vp, ctypes.c_size_t, _vp]
@@ -200,6 +202,19 @@ def moe_permute(x, expert_ids, T, H, K, num_experts, permuted, sorted_slot, row_
         _ptr(row_of_slot, _I32, "row_of_slot"), _ptr(expert_counts, _I32, "expert_counts"),
         _ptr(expert_offsets, _I32, "expert_offsets"), _ptr(ws, None, "workspace"),
         ws.numel() if ws is not None else 0, _stream(stream)), "moe_permute")
+
+
+def moe_permute_noalloc(x, expert_ids, T, H, K, num_experts, permuted, sorted_slot, row_of_slot,
+                        expert_counts, expert_offsets, stream=None, *, active_mask=None):
+    """moe_permute without a workspace: the library's own per-GPU array holds the
+    count table (calls overlapping in time on one GPU must not be issued)."""
+    mp, per_slot = _mask(active_mask, T, K)
+    _check(load().moe_permute_noalloc(
+        _ptr(x, _BF16, "x"), _ptr(expert_ids, _I32, "expert_ids"), mp, per_slot, T, H, K,
+        num_experts,
+        _ptr(permuted, _BF16, "permuted"), _ptr(sorted_slot, _I32, "sorted_slot"),
+        _ptr(row_of_slot, _I32, "row_of_slot"), _ptr(expert_counts, _I32, "expert_counts"),
+        _ptr(expert_offsets, _I32, "expert_offsets"), _stream(stream)), "moe_permute_noalloc")
 
 
 def moe_rank_to_expert_reorder(x_rank_major, counts, R, E_local, N, H, y_expert_major, perm,

@@ -396,7 +396,7 @@ def run_ops(args, dev, flush):
         di["counts_by_dest"], di["total"], wsi)
     src, coeff = dbf(g["outer_output"], dev), dt(g["router_coeff"], dev)
     wb = torch.empty((G, H), dtype=torch.bfloat16, device=dev)
-    wsc = moe.workspace(moe.moe_deredundency_combine_workspace_size(G), dev)
+    wsc = moe.workspace(moe.moe_deredundency_combine_workspace_size(n_sel, G), dev)
     f_dc = lambda: moe.moe_deredundency_combine(src, coeff, di["indices"], n_sel, H, G, wb, wsc)
     ops.append(dict(workload=c["name"], **op_entry(
         "deredundency_dispatch_indices", *time_op(f_di, args.op_iters, flush),

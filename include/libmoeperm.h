@@ -424,24 +424,25 @@ moe_status_t moe_deredundency_dispatch_indices(
  * [EP] _scale_by_router_coeff then _scatter_add_first_dim: outer_output row j
  * is scaled by router_coeff[j] and added into a zero [G, H] buffer at row
  * dispatch_indices[j]:
- *     whiteboard[r] = bf16( router_coeff[j] * outer_output[j] )  if dispatch_indices[j] == r
- *                   = 0                                           if no j names r
- * (the product correctly rounded; router_coeff NULL: the rows are copied).
- * As in a zero buffer plus the row, an exactly zero product is +0.
- * The dispatch indices of moe_deredundency_dispatch_indices name every row at
- * most once, which this call requires: two j naming the same row leave one of
- * the two scaled rows there, not their sum. Indices outside [0, G) are skipped.
- * Every row of the whiteboard is written once (no separate zero fill).
+ *     whiteboard[r] = bf16( sum over j with dispatch_indices[j] == r of
+ *                           router_coeff[j] * outer_output[j] ),  0 if no j names r
+ * (router_coeff NULL: coefficient 1). A row named once holds the correctly
+ * rounded product; a row named by several j holds their sum accumulated in
+ * fp32 in ascending j, rounded once; either way the result does not depend on
+ * scheduling. As in a zero buffer plus the rows, an exactly zero result is +0.
+ * The indices of moe_deredundency_dispatch_indices name every row at most
+ * once. Indices outside [0, G) are skipped. Every row of the whiteboard is
+ * written once (no separate zero fill).
  *
  *  outer_output     bf16 [n, H]  in
  *  router_coeff     fp32 [n]     in  (nullable)
  *  dispatch_indices int32 [n]    in
  *  whiteboard       bf16 [G, H]  out
- *  workspace        moe_deredundency_combine_workspace_size(G) bytes
+ *  workspace        moe_deredundency_combine_workspace_size(n, G) bytes
  * Errors: INVALID_ARG for n or G outside [0, INT32_MAX], H <= 0, NULL /
  * misaligned pointers; UNSUPPORTED for H % 8 != 0; WORKSPACE if too small.
  * ------------------------------------------------------------------------ */
-moe_status_t moe_deredundency_combine_workspace_size(int64_t G, size_t* bytes);
+moe_status_t moe_deredundency_combine_workspace_size(int64_t n, int64_t G, size_t* bytes);
 moe_status_t moe_deredundency_combine(const void* outer_output, const float* router_coeff,
                                       const int32_t* dispatch_indices, int64_t n, int32_t H,
                                       int64_t G, void* whiteboard, void* workspace,

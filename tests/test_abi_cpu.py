@@ -58,7 +58,7 @@ def test_status_strings_and_version(lib):
     assert binding.status_str(0) == "MOE_OK"
     assert binding.status_str(3) == "MOE_ERR_WORKSPACE"
     assert binding.status_str(99) == "MOE_ERR_UNKNOWN"
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
 
 
 def test_workspace_sizes(lib):
@@ -320,6 +320,15 @@ def test_dered_checks(lib):
     assert comb(wb=None) == INVALID
     assert comb(ws=None) == WORKSPACE
     assert comb(wsb=4) == WORKSPACE
+    # the workspace holds the per-row counts and segment starts and the source list
+    from unpermute_combine_moe_amd import binding as b
+    small = b.moe_deredundency_combine_workspace_size(10, 20)
+    assert small >= 4 * (20 + 21 + 10)
+    assert b.moe_deredundency_combine_workspace_size(1000, 20) > small
+    assert comb(wsb=small - 4) == WORKSPACE
+    for n, G in ((-1, 5), (5, -1), (2**31, 5)):
+        with pytest.raises(b.MoeError):
+            b.moe_deredundency_combine_workspace_size(n, G)
 
 
 def test_binding_rejects_wrong_tensors(lib):

@@ -1,6 +1,9 @@
 """GPU parity of the deredundency calls against the oracle: dispatch indices,
-counts and total bit-exact; the whiteboard bit-exact (a correctly rounded
-product per row on both sides, zero rows elsewhere)."""
+counts and total bit-exact; the whiteboard bit-exact where a row has at most
+one source (a correctly rounded product per row on both sides, zero rows
+elsewhere), and where several sources land on one row (the page's scatter-add
+accumulates them) within the 1e-2 relative bound of the fp64 sum, and the same
+bits on every run."""
 import json
 import os
 
@@ -10,7 +13,7 @@ import torch
 
 import moe_workloads as W
 import oracle
-from helpers import bits, to_dev, to_dev_bf16
+from helpers import assert_rel, bits, f64, to_dev, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -115,3 +118,45 @@ def test_dered_workload_end_to_end(moe_lib):
     torch.cuda.synchronize()
     ref, _ = oracle.scatter_add_rows(d["outer_output"], idx, d["G"], d["router_coeff"])
     np.testing.assert_array_equal(bits(wb), ref)
+
+
+def _combine_dup(moe, src, coeff, idx, G):
+    """Whiteboard with repeated indices: rows with one source bit-exact, rows
+    with several within 1e-2 of the fp64 sum; two runs give the same bits."""
+    n, H = src.shape
+    G_ok = (idx >= 0) & (idx < G)
+    mult = np.bincount(idx[G_ok], minlength=G)
+    print(f"dered combine n={n} H={H} G={G} max sources per row {mult.max()}", flush=True)
+    args = (to_dev_bf16(src), to_dev(coeff) if coeff is not None else None, to_dev(idx))
+    wb1 = bits(moe.dered_combine_alloc(*args, G))
+    wb2 = bits(moe.dered_combine_alloc(*args, G))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(wb1, wb2)
+    ref, ref64 = oracle.scatter_add_rows(src, idx, G, coeff)
+    single = mult <= 1
+    np.testing.assert_array_equal(wb1[single], ref[single])
+    assert_rel(f64(wb1[~single]), ref64[~single], 1e-2, "rows with several sources")
+
+
+def test_dered_combine_duplicates(moe_lib):
+    rng = np.random.default_rng(11)
+    n, G, H = 600, 150, 136                      # ~4 sources per row, H/8 = 17 chunks
+    src = W.normal_bf16(rng, (n, H))
+    idx = rng.integers(0, G, size=n).astype(np.int32)
+    idx[::37] = G + 2                            # skipped
+    idx[::41] = -1                               # skipped
+    coeff = rng.standard_normal(n).astype(np.float32)
+    _combine_dup(moe_lib, src, coeff, idx, G)
+    _combine_dup(moe_lib, src, None, idx, G)
+
+
+def test_dered_combine_long_segment(moe_lib):
+    """One row named by 200 sources (more than a wave's lanes), the others by
+    at most one; H = 2064 takes the row in several passes of the wave."""
+    rng = np.random.default_rng(12)
+    n, G, H = 260, 80, 2064
+    src = W.normal_bf16(rng, (n, H))
+    idx = np.concatenate([np.full(200, 7), rng.permutation(np.delete(np.arange(G), 7))[:60]])
+    idx = rng.permutation(idx).astype(np.int32)
+    coeff = rng.uniform(0.5, 1.5, n).astype(np.float32)
+    _combine_dup(moe_lib, src, coeff, idx, G)

@@ -93,7 +93,7 @@ def load(path: str = LIB_PATH):
     lib.moe_deredundency_dispatch_indices_workspace_size.argtypes = [_i32, _i32, _i32, _i32, sz]
     lib.moe_deredundency_dispatch_indices.argtypes = [_vp, _i32, _i32, _i32, _i32, _i32, _i64,
                                                       _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
-    lib.moe_deredundency_combine_workspace_size.argtypes = [_i64, sz]
+    lib.moe_deredundency_combine_workspace_size.argtypes = [_i64, _i64, sz]
     lib.moe_deredundency_combine.argtypes = [_vp, _vp, _vp, _i64, _i32, _i64, _vp, _vp,
                                              ctypes.c_size_t, _vp]
     lib.moe_grouped_gemm_swiglu_grad_workspace_size.argtypes = [_i32, _i64, _i32, _i32, sz]
@@ -308,11 +308,11 @@ def moe_deredundency_dispatch_indices(tokens_per_expert_by_source, oep_size, num
         ws.numel() if ws is not None else 0, _stream(stream)), "moe_deredundency_dispatch_indices")
 
 
-def moe_deredundency_combine_workspace_size(G) -> int:
-    n = ctypes.c_size_t(0)
-    _check(load().moe_deredundency_combine_workspace_size(G, ctypes.byref(n)),
+def moe_deredundency_combine_workspace_size(n, G) -> int:
+    b = ctypes.c_size_t(0)
+    _check(load().moe_deredundency_combine_workspace_size(n, G, ctypes.byref(b)),
            "moe_deredundency_combine_workspace_size")
-    return n.value
+    return b.value
 
 
 def moe_deredundency_combine(outer_output, router_coeff, dispatch_indices, n, H, G, whiteboard, ws,
@@ -478,7 +478,7 @@ def dered_indices_alloc(tokens_per_expert_by_source, expert_start, iep_size, num
 def dered_combine_alloc(outer_output, router_coeff, dispatch_indices, G, *, stream=None):
     n, H = outer_output.shape
     wb = torch.empty((G, H), dtype=_BF16, device=outer_output.device)
-    ws = workspace(moe_deredundency_combine_workspace_size(G), outer_output.device)
+    ws = workspace(moe_deredundency_combine_workspace_size(n, G), outer_output.device)
     moe_deredundency_combine(outer_output, router_coeff, dispatch_indices, n, H, G, wb, ws, stream)
     return wb
 

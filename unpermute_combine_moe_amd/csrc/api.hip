@@ -13,7 +13,7 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 1;
+constexpr int32_t kAbiVersion = 2;
 
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 // a row tensor: non-null and 16-byte aligned
@@ -401,9 +401,11 @@ MOE_API moe_status_t moe_deredundency_dispatch_indices(
                                               indices, counts_by_dest, total, workspace, stream));
 }
 
-MOE_API moe_status_t moe_deredundency_combine_workspace_size(int64_t G, size_t* bytes) {
-  if (bytes == nullptr || G < 0 || G > INT32_MAX) return MOE_ERR_INVALID_ARG;
-  *bytes = moe::dered_combine_workspace_bytes(G);
+MOE_API moe_status_t moe_deredundency_combine_workspace_size(int64_t n, int64_t G,
+                                                             size_t* bytes) {
+  if (bytes == nullptr || n < 0 || n > INT32_MAX || G < 0 || G > INT32_MAX)
+    return MOE_ERR_INVALID_ARG;
+  *bytes = moe::dered_combine_workspace_bytes(n, G);
   return MOE_OK;
 }
 
@@ -418,7 +420,7 @@ MOE_API moe_status_t moe_deredundency_combine(const void* outer_output, const fl
   if (router_coeff != nullptr && !aligned(router_coeff, 4)) return MOE_ERR_INVALID_ARG;
   if (G > 0 && !row_ok(whiteboard)) return MOE_ERR_INVALID_ARG;
   if (G > 0 && (workspace == nullptr || !aligned(workspace, 4) ||
-                workspace_bytes < moe::dered_combine_workspace_bytes(G)))
+                workspace_bytes < moe::dered_combine_workspace_bytes(n, G)))
     return MOE_ERR_WORKSPACE;
   return hip_status(moe::launch_dered_combine(u16(outer_output), router_coeff, dispatch_indices, n,
                                               H, G, u16(whiteboard), workspace, stream));

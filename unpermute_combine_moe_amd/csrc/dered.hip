@@ -14,10 +14,16 @@
 // gathered row of every (source, expert) block) and the selected blocks in
 // destination order; the index kernel then gives every output position its
 // block by binary search, as the reorder does.
-// Whiteboard: the dispatch indices are distinct (a selection of gathered
-// rows), so the scatter-add is inverted into a gather: inv[r] = j for
-// indices[j] = r, and every whiteboard row is written exactly once -- the
-// scaled source row, or zeros. No atomics, no separate zero fill of the rows.
+// Whiteboard: the scatter-add is turned into a segmented gather by destination
+// row. Each row's sources are counted (integer atomics: the counts do not
+// depend on the order), an exclusive scan of the counts gives each row its
+// segment of a source list, and every source index is placed in its row's
+// segment. One wave per whiteboard row then writes the row once: zeros for no
+// source, the correctly rounded scaled row for one source (the common case:
+// the dispatch indices name distinct rows), and for several sources their
+// scaled rows summed in fp32 in ascending source order (the order the
+// page's scatter-add applies them), rounded once. No floating-point atomics,
+// so the result does not depend on scheduling.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -87,18 +93,95 @@ k_dered_index(const int32_t* __restrict__ ws, int64_t F, int B, int64_t capacity
   indices[i] = v;
 }
 
+// ---------------------------------------------------------------- whiteboard
+// ws layout (int32): cnt[G] | start[G + 1] | bsum[nb] | list[n],
+// nb = ceil(G / kScanBlock)
+constexpr int kScanThreads = 256;
+constexpr int kScanPer = 16;
+constexpr int kScanBlock = kScanThreads * kScanPer;
+
 __global__ void __launch_bounds__(kIndexThreads)
-k_inv_fill(int32_t* __restrict__ inv, int64_t G) {
+k_wb_clear(int32_t* __restrict__ cnt, int64_t G) {
   const int64_t r = int64_t(blockIdx.x) * kIndexThreads + threadIdx.x;
-  if (r < G) inv[r] = -1;
+  if (r < G) cnt[r] = 0;
 }
 
 __global__ void __launch_bounds__(kIndexThreads)
-k_inv_scatter(const int32_t* __restrict__ indices, int64_t n, int64_t G, int32_t* __restrict__ inv) {
+k_wb_count(const int32_t* __restrict__ indices, int64_t n, int64_t G, int32_t* __restrict__ cnt) {
   const int64_t j = int64_t(blockIdx.x) * kIndexThreads + threadIdx.x;
   if (j >= n) return;
   const int64_t r = indices[j];
-  if (r >= 0 && r < G) inv[r] = static_cast<int32_t>(j);
+  if (r >= 0 && r < G) atomicAdd(&cnt[r], 1);
+}
+
+// Sum of each block of kScanBlock counts.
+__global__ void __launch_bounds__(kScanThreads)
+k_wb_block_sums(const int32_t* __restrict__ cnt, int64_t G, int32_t* __restrict__ bsum) {
+  __shared__ int32_t part[kScanThreads];
+  const int64_t base = int64_t(blockIdx.x) * kScanBlock + int64_t(threadIdx.x) * kScanPer;
+  int32_t v = 0;
+#pragma unroll
+  for (int i = 0; i < kScanPer; ++i) v += (base + i < G) ? cnt[base + i] : 0;
+  part[threadIdx.x] = v;
+  __syncthreads();
+  for (int o = kScanThreads / 2; o > 0; o >>= 1) {
+    if (static_cast<int>(threadIdx.x) < o) part[threadIdx.x] += part[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) bsum[blockIdx.x] = part[0];
+}
+
+// Exclusive scan of the block sums in place (one workgroup).
+__global__ void __launch_bounds__(1024) k_wb_scan_sums(int32_t* __restrict__ bsum, int64_t nb) {
+  __shared__ int32_t part[1024];
+  block_exclusive_scan<1024>(bsum, bsum, nb, part);
+}
+
+// start[r] = exclusive prefix of cnt; start[G] = number of placed sources.
+// cnt is cleared again, to count the placements.
+__global__ void __launch_bounds__(kScanThreads)
+k_wb_block_scan(int32_t* __restrict__ cnt, int64_t G, const int32_t* __restrict__ bsum,
+                int32_t* __restrict__ start) {
+  __shared__ int32_t part[kScanThreads];
+  const int64_t base = int64_t(blockIdx.x) * kScanBlock + int64_t(threadIdx.x) * kScanPer;
+  int32_t v[kScanPer];
+  int32_t sum = 0;
+#pragma unroll
+  for (int i = 0; i < kScanPer; ++i) {
+    v[i] = (base + i < G) ? cnt[base + i] : 0;
+    sum += v[i];
+  }
+  part[threadIdx.x] = sum;
+  __syncthreads();
+  for (int o = 1; o < kScanThreads; o <<= 1) {
+    const int32_t x = static_cast<int>(threadIdx.x) >= o ? part[threadIdx.x - o] : 0;
+    __syncthreads();
+    part[threadIdx.x] += x;
+    __syncthreads();
+  }
+  int32_t run = bsum[blockIdx.x] + part[threadIdx.x] - sum;
+#pragma unroll
+  for (int i = 0; i < kScanPer; ++i) {
+    if (base + i < G) {
+      start[base + i] = run;
+      cnt[base + i] = 0;
+    }
+    run += v[i];
+    if (base + i == G - 1) start[G] = run;
+  }
+}
+
+// Every source index into its row's segment (order inside a segment is
+// arbitrary here; the row kernel reads a segment in ascending source order).
+__global__ void __launch_bounds__(kIndexThreads)
+k_wb_place(const int32_t* __restrict__ indices, int64_t n, int64_t G,
+           const int32_t* __restrict__ start, int32_t* __restrict__ fill,
+           int32_t* __restrict__ list) {
+  const int64_t j = int64_t(blockIdx.x) * kIndexThreads + threadIdx.x;
+  if (j >= n) return;
+  const int64_t r = indices[j];
+  if (r < 0 || r >= G) return;
+  list[start[r] + atomicAdd(&fill[r], 1)] = static_cast<int32_t>(j);
 }
 
 // A whiteboard element is 0 + coeff * value, added into a zero buffer: an
@@ -116,23 +199,10 @@ __device__ __forceinline__ uint32_t scaled_bf16(float p, float v) {
   return (p == 0.0f || v == 0.0f) ? 0u : mul_to_bf16_exact(p, v);
 }
 
-// One wave per whiteboard row: the scaled source row (correctly rounded
-// product of the fp32 coefficient and the bf16 value) or zeros.
-__global__ void __launch_bounds__(kRowWaves * kWave)
-k_whiteboard_rows(const uint16_t* __restrict__ src, const float* __restrict__ coeff,
-                  const int32_t* __restrict__ inv, int64_t G, int H, uint16_t* __restrict__ wb) {
-  const int64_t r = uniform(static_cast<int>(blockIdx.x * kRowWaves + threadIdx.x / kWave));
-  if (r >= G) return;
-  const int lane = threadIdx.x % kWave;
-  const int64_t j = inv[r];
-  const int chunks = H / 8;
-  uint16_t* dst = wb + r * H;
-  if (j < 0) {
-    const Vec8 z{{0u, 0u, 0u, 0u}};
-    for (int c = lane; c < chunks; c += kWave) store16_nt(dst + c * 8, z);
-    return;
-  }
-  const uint16_t* s = src + j * H;
+// One source: the scaled row (correctly rounded product of the fp32
+// coefficient and the bf16 value), or the row itself without coefficients.
+__device__ void wb_single_row(const uint16_t* __restrict__ s, const float* __restrict__ coeff,
+                              int64_t j, int chunks, int lane, uint16_t* __restrict__ dst) {
   if (coeff == nullptr) {
     for (int c = lane; c < chunks; c += kWave) {
       Vec8 v = load16_nt(s + c * 8);
@@ -166,6 +236,83 @@ k_whiteboard_rows(const uint16_t* __restrict__ src, const float* __restrict__ co
   }
 }
 
+// The q-th smallest source index of a segment of L > 1 entries. Up to 64
+// entries sit one per lane (rank by comparison with every other lane); longer
+// segments are walked by repeatedly taking the smallest index above the
+// previous one (indices in a segment are distinct).
+__device__ int32_t wb_nth(const int32_t* __restrict__ seg, int L, int q, int32_t prev, int lane,
+                          int32_t mine, int rank) {
+  if (L <= kWave) {
+    const uint64_t hit = ballot(lane < L && rank == q);
+    return __shfl(mine, static_cast<int>(__builtin_ctzll(hit)), kWave);
+  }
+  int32_t best = INT32_MAX;
+  for (int i = lane; i < L; i += kWave) {
+    const int32_t v = seg[i];
+    if (v > prev && v < best) best = v;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) best = std::min(best, __shfl_xor(best, o, kWave));
+  return best;
+}
+
+// One wave per whiteboard row.
+constexpr int kWbSumChunks = 4;  // 16-byte chunks per lane accumulated per pass
+__global__ void __launch_bounds__(kRowWaves * kWave)
+k_whiteboard_rows(const uint16_t* __restrict__ src, const float* __restrict__ coeff,
+                  const int32_t* __restrict__ start, const int32_t* __restrict__ list, int64_t G,
+                  int H, uint16_t* __restrict__ wb) {
+  const int64_t r = uniform(static_cast<int>(blockIdx.x * kRowWaves + threadIdx.x / kWave));
+  if (r >= G) return;
+  const int lane = threadIdx.x % kWave;
+  const int32_t s0 = uniform(start[r]);
+  const int L = uniform(start[r + 1] - s0);
+  const int chunks = H / 8;
+  uint16_t* dst = wb + r * H;
+  if (L == 0) {
+    const Vec8 z{{0u, 0u, 0u, 0u}};
+    for (int c = lane; c < chunks; c += kWave) store16_nt(dst + c * 8, z);
+    return;
+  }
+  const int32_t* seg = list + s0;
+  if (L == 1) {
+    wb_single_row(src + int64_t(seg[0]) * H, coeff, seg[0], chunks, lane, dst);
+    return;
+  }
+  // several sources: ranks of the first 64 entries (used when L <= 64)
+  const int32_t mine = lane < L ? seg[lane] : INT32_MAX;
+  int rank = 0;
+  for (int i = 0; i < std::min(L, kWave); ++i) rank += (__shfl(mine, i, kWave) < mine) ? 1 : 0;
+  for (int c0 = 0; c0 < chunks; c0 += kWave * kWbSumChunks) {
+    float acc[kWbSumChunks][8];
+#pragma unroll
+    for (int b = 0; b < kWbSumChunks; ++b)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[b][i] = 0.f;
+    int32_t prev = -1;
+    for (int q = 0; q < L; ++q) {
+      const int32_t j = wb_nth(seg, L, q, prev, lane, mine, rank);
+      prev = j;
+      const float p = coeff ? coeff[j] : 1.0f;
+      const uint16_t* s = src + int64_t(j) * H;
+#pragma unroll
+      for (int b = 0; b < kWbSumChunks; ++b) {
+        const int c = c0 + b * kWave + lane;
+        if (c >= chunks) continue;
+        float f[8];
+        unpack8(load16(s + c * 8), f);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[b][i] = __builtin_fmaf(p, f[i], acc[b][i]);
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < kWbSumChunks; ++b) {
+      const int c = c0 + b * kWave + lane;
+      if (c < chunks) store16_nt(dst + c * 8, pack8(acc[b]));
+    }
+  }
+}
+
 }  // namespace
 
 size_t dered_indices_workspace_bytes(int oep, int E, int iep, int El) {
@@ -187,22 +334,35 @@ hipError_t launch_dered_indices(const int32_t* counts, int oep, int E, int exper
   return hipGetLastError();
 }
 
-size_t dered_combine_workspace_bytes(int64_t G) {
-  return static_cast<size_t>(G > 0 ? G : 1) * sizeof(int32_t);
+size_t dered_combine_workspace_bytes(int64_t n, int64_t G) {
+  const int64_t nb = ceil_div(G, kScanBlock);
+  return static_cast<size_t>(G + (G + 1) + nb + n + 1) * sizeof(int32_t);
 }
 
 hipError_t launch_dered_combine(const uint16_t* src, const float* coeff, const int32_t* indices,
                                 int64_t n, int H, int64_t G, uint16_t* wb, void* ws,
                                 hipStream_t st) {
   if (G == 0) return hipGetLastError();
-  int32_t* inv = static_cast<int32_t*>(ws);
-  hipLaunchKernelGGL(k_inv_fill, dim3(static_cast<unsigned>(ceil_div(G, kIndexThreads))),
-                     dim3(kIndexThreads), 0, st, inv, G);
+  const int64_t nb = ceil_div(G, kScanBlock);
+  int32_t* cnt = static_cast<int32_t*>(ws);
+  int32_t* start = cnt + G;
+  int32_t* bsum = start + (G + 1);
+  int32_t* list = bsum + nb;
+  const dim3 gG(static_cast<unsigned>(ceil_div(G, kIndexThreads)));
+  hipLaunchKernelGGL(k_wb_clear, gG, dim3(kIndexThreads), 0, st, cnt, G);
   if (n > 0)
-    hipLaunchKernelGGL(k_inv_scatter, dim3(static_cast<unsigned>(ceil_div(n, kIndexThreads))),
-                       dim3(kIndexThreads), 0, st, indices, n, G, inv);
+    hipLaunchKernelGGL(k_wb_count, dim3(static_cast<unsigned>(ceil_div(n, kIndexThreads))),
+                       dim3(kIndexThreads), 0, st, indices, n, G, cnt);
+  hipLaunchKernelGGL(k_wb_block_sums, dim3(static_cast<unsigned>(nb)), dim3(kScanThreads), 0, st,
+                     cnt, G, bsum);
+  hipLaunchKernelGGL(k_wb_scan_sums, dim3(1), dim3(1024), 0, st, bsum, nb);
+  hipLaunchKernelGGL(k_wb_block_scan, dim3(static_cast<unsigned>(nb)), dim3(kScanThreads), 0, st,
+                     cnt, G, bsum, start);
+  if (n > 0)
+    hipLaunchKernelGGL(k_wb_place, dim3(static_cast<unsigned>(ceil_div(n, kIndexThreads))),
+                       dim3(kIndexThreads), 0, st, indices, n, G, start, cnt, list);
   hipLaunchKernelGGL(k_whiteboard_rows, dim3(static_cast<unsigned>(ceil_div(G, kRowWaves))),
-                     dim3(kRowWaves * kWave), 0, st, src, coeff, inv, G, H, wb);
+                     dim3(kRowWaves * kWave), 0, st, src, coeff, start, list, G, H, wb);
   return hipGetLastError();
 }
 

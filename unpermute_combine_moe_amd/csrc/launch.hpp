@@ -84,7 +84,7 @@ hipError_t launch_dered_indices(const int32_t* counts, int oep, int E, int exper
                                 int El, int64_t capacity, int32_t* indices,
                                 int32_t* counts_by_dest, int32_t* total, void* ws,
                                 hipStream_t st);
-size_t dered_combine_workspace_bytes(int64_t G);
+size_t dered_combine_workspace_bytes(int64_t n, int64_t G);
 hipError_t launch_dered_combine(const uint16_t* src, const float* coeff, const int32_t* indices,
                                 int64_t n, int H, int64_t G, uint16_t* wb, void* ws,
                                 hipStream_t st);

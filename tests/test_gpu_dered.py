@@ -160,3 +160,16 @@ def test_dered_combine_long_segment(moe_lib):
     idx = rng.permutation(idx).astype(np.int32)
     coeff = rng.uniform(0.5, 1.5, n).astype(np.float32)
     _combine_dup(moe_lib, src, coeff, idx, G)
+
+
+def test_dered_combine_many_rows(moe_lib):
+    """More rows than the one-workgroup scan takes (65,536): the three-kernel
+    scan of the per-row counts, with repeated and out-of-range indices."""
+    rng = np.random.default_rng(13)
+    n, G, H = 3000, 70_001, 8
+    src = W.normal_bf16(rng, (n, H))
+    idx = rng.integers(0, G, size=n).astype(np.int32)
+    idx[:40] = idx[40:80]                        # 40 rows named twice
+    idx[100] = G                                 # skipped
+    coeff = rng.standard_normal(n).astype(np.float32)
+    _combine_dup(moe_lib, src, coeff, idx, G)

@@ -18,7 +18,8 @@
 // row. Each row's sources are counted (integer atomics: the counts do not
 // depend on the order), an exclusive scan of the counts gives each row its
 // segment of a source list, and every source index is placed in its row's
-// segment. One wave per whiteboard row then writes the row once: zeros for no
+// segment (the scan is one workgroup up to 65,536 rows, three kernels beyond).
+// One wave per whiteboard row then writes the row once: zeros for no
 // source, the correctly rounded scaled row for one source (the common case:
 // the dispatch indices name distinct rows), and for several sources their
 // scaled rows summed in fp32 in ascending source order (the order the
@@ -94,16 +95,20 @@ k_dered_index(const int32_t* __restrict__ ws, int64_t F, int B, int64_t capacity
 }
 
 // ---------------------------------------------------------------- whiteboard
-// ws layout (int32): cnt[G] | start[G + 1] | bsum[nb] | list[n],
-// nb = ceil(G / kScanBlock)
+// ws layout (int32): cnt[G] | start[G + 1] | one[G] | bsum[nb] | list[n],
+// nb = ceil(G / kScanBlock); one[r] = the single source of row r, -1 for none,
+// -2 for several (the row kernel's one-load path for the common case)
 constexpr int kScanThreads = 256;
 constexpr int kScanPer = 16;
 constexpr int kScanBlock = kScanThreads * kScanPer;
 
 __global__ void __launch_bounds__(kIndexThreads)
-k_wb_clear(int32_t* __restrict__ cnt, int64_t G) {
+k_wb_clear(int32_t* __restrict__ cnt, int32_t* __restrict__ one, int64_t G) {
   const int64_t r = int64_t(blockIdx.x) * kIndexThreads + threadIdx.x;
-  if (r < G) cnt[r] = 0;
+  if (r < G) {
+    cnt[r] = 0;
+    one[r] = -1;
+  }
 }
 
 __global__ void __launch_bounds__(kIndexThreads)
@@ -171,17 +176,81 @@ k_wb_block_scan(int32_t* __restrict__ cnt, int64_t G, const int32_t* __restrict_
   }
 }
 
+// The whole scan in one workgroup, for up to kOneScanMax rows. Each of the 16
+// waves owns a contiguous segment of the counts and reads it 64 at a time
+// (one coalesced row per step, kept in registers); the wave totals are
+// scanned in LDS, then each wave walks its rows again in order, carrying the
+// running prefix with a wave-level inclusive scan per row. start[r] is the
+// exclusive prefix, start[G] the total; cnt is cleared for the placement.
+constexpr int kOneWaves = 16;
+constexpr int kOneRows = 64;   // 64-element rows per wave
+constexpr int kOneBatch = 16;  // rows loaded together
+constexpr int64_t kOneScanMax = int64_t(kOneWaves) * kOneRows * kWave;
+__global__ void __launch_bounds__(kOneWaves * kWave)
+k_wb_scan_one(int32_t* __restrict__ cnt, int64_t G64, int32_t* __restrict__ start) {
+  __shared__ int32_t wsum[kOneWaves];
+  const int G = static_cast<int>(G64);  // <= kOneScanMax
+  const int w = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int rows = static_cast<int>(ceil_div(G, kOneWaves * kWave));  // rows per wave
+  const int b0 = w * rows * kWave;
+  int32_t tot = 0;
+  for (int i0 = 0; i0 < rows; i0 += kOneBatch) {
+    int32_t v[kOneBatch];
+#pragma unroll
+    for (int i = 0; i < kOneBatch; ++i) {
+      const int r = b0 + (i0 + i) * kWave + lane;
+      v[i] = (i0 + i < rows && r < G) ? cnt[r] : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < kOneBatch; ++i) tot += v[i];
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) tot += __shfl_xor(tot, o, kWave);
+  if (lane == 0) wsum[w] = tot;
+  __syncthreads();
+  int32_t carry = 0;
+  for (int ww = 0; ww < w; ++ww) carry += wsum[ww];
+  for (int i0 = 0; i0 < rows; i0 += kOneBatch) {
+    int32_t v[kOneBatch];
+#pragma unroll
+    for (int i = 0; i < kOneBatch; ++i) {
+      const int r = b0 + (i0 + i) * kWave + lane;
+      v[i] = (i0 + i < rows && r < G) ? cnt[r] : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < kOneBatch; ++i) {
+      if (i0 + i >= rows) break;
+      const int r = b0 + (i0 + i) * kWave + lane;
+      int32_t incl = v[i];
+#pragma unroll
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int32_t x = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += x;
+      }
+      if (r < G) {
+        start[r] = carry + incl - v[i];
+        cnt[r] = 0;
+      }
+      carry += __shfl(incl, kWave - 1, kWave);
+    }
+  }
+  if (w == kOneWaves - 1 && lane == 0) start[G] = carry;
+}
+
 // Every source index into its row's segment (order inside a segment is
 // arbitrary here; the row kernel reads a segment in ascending source order).
 __global__ void __launch_bounds__(kIndexThreads)
 k_wb_place(const int32_t* __restrict__ indices, int64_t n, int64_t G,
            const int32_t* __restrict__ start, int32_t* __restrict__ fill,
-           int32_t* __restrict__ list) {
+           int32_t* __restrict__ list, int32_t* __restrict__ one) {
   const int64_t j = int64_t(blockIdx.x) * kIndexThreads + threadIdx.x;
   if (j >= n) return;
   const int64_t r = indices[j];
   if (r < 0 || r >= G) return;
-  list[start[r] + atomicAdd(&fill[r], 1)] = static_cast<int32_t>(j);
+  const int32_t s0 = start[r];
+  list[s0 + atomicAdd(&fill[r], 1)] = static_cast<int32_t>(j);
+  // every source of a row with several writes the same -2
+  one[r] = (start[r + 1] - s0 == 1) ? static_cast<int32_t>(j) : -2;
 }
 
 // A whiteboard element is 0 + coeff * value, added into a zero buffer: an
@@ -260,25 +329,26 @@ __device__ int32_t wb_nth(const int32_t* __restrict__ seg, int L, int q, int32_t
 constexpr int kWbSumChunks = 4;  // 16-byte chunks per lane accumulated per pass
 __global__ void __launch_bounds__(kRowWaves * kWave)
 k_whiteboard_rows(const uint16_t* __restrict__ src, const float* __restrict__ coeff,
-                  const int32_t* __restrict__ start, const int32_t* __restrict__ list, int64_t G,
-                  int H, uint16_t* __restrict__ wb) {
+                  const int32_t* __restrict__ start, const int32_t* __restrict__ list,
+                  const int32_t* __restrict__ one, int64_t G, int H, uint16_t* __restrict__ wb) {
   const int64_t r = uniform(static_cast<int>(blockIdx.x * kRowWaves + threadIdx.x / kWave));
   if (r >= G) return;
   const int lane = threadIdx.x % kWave;
-  const int32_t s0 = uniform(start[r]);
-  const int L = uniform(start[r + 1] - s0);
+  const int32_t j1 = uniform(one[r]);
   const int chunks = H / 8;
   uint16_t* dst = wb + r * H;
-  if (L == 0) {
+  if (j1 == -1) {
     const Vec8 z{{0u, 0u, 0u, 0u}};
     for (int c = lane; c < chunks; c += kWave) store16_nt(dst + c * 8, z);
     return;
   }
-  const int32_t* seg = list + s0;
-  if (L == 1) {
-    wb_single_row(src + int64_t(seg[0]) * H, coeff, seg[0], chunks, lane, dst);
+  if (j1 >= 0) {
+    wb_single_row(src + int64_t(j1) * H, coeff, j1, chunks, lane, dst);
     return;
   }
+  const int32_t s0 = uniform(start[r]);
+  const int L = uniform(start[r + 1] - s0);
+  const int32_t* seg = list + s0;
   // several sources: ranks of the first 64 entries (used when L <= 64)
   const int32_t mine = lane < L ? seg[lane] : INT32_MAX;
   int rank = 0;
@@ -336,7 +406,7 @@ hipError_t launch_dered_indices(const int32_t* counts, int oep, int E, int exper
 
 size_t dered_combine_workspace_bytes(int64_t n, int64_t G) {
   const int64_t nb = ceil_div(G, kScanBlock);
-  return static_cast<size_t>(G + (G + 1) + nb + n + 1) * sizeof(int32_t);
+  return static_cast<size_t>(G + (G + 1) + G + nb + n + 1) * sizeof(int32_t);
 }
 
 hipError_t launch_dered_combine(const uint16_t* src, const float* coeff, const int32_t* indices,
@@ -346,23 +416,28 @@ hipError_t launch_dered_combine(const uint16_t* src, const float* coeff, const i
   const int64_t nb = ceil_div(G, kScanBlock);
   int32_t* cnt = static_cast<int32_t*>(ws);
   int32_t* start = cnt + G;
-  int32_t* bsum = start + (G + 1);
+  int32_t* one = start + (G + 1);
+  int32_t* bsum = one + G;
   int32_t* list = bsum + nb;
   const dim3 gG(static_cast<unsigned>(ceil_div(G, kIndexThreads)));
-  hipLaunchKernelGGL(k_wb_clear, gG, dim3(kIndexThreads), 0, st, cnt, G);
+  hipLaunchKernelGGL(k_wb_clear, gG, dim3(kIndexThreads), 0, st, cnt, one, G);
   if (n > 0)
     hipLaunchKernelGGL(k_wb_count, dim3(static_cast<unsigned>(ceil_div(n, kIndexThreads))),
                        dim3(kIndexThreads), 0, st, indices, n, G, cnt);
-  hipLaunchKernelGGL(k_wb_block_sums, dim3(static_cast<unsigned>(nb)), dim3(kScanThreads), 0, st,
-                     cnt, G, bsum);
-  hipLaunchKernelGGL(k_wb_scan_sums, dim3(1), dim3(1024), 0, st, bsum, nb);
-  hipLaunchKernelGGL(k_wb_block_scan, dim3(static_cast<unsigned>(nb)), dim3(kScanThreads), 0, st,
-                     cnt, G, bsum, start);
+  if (G <= kOneScanMax) {
+    hipLaunchKernelGGL(k_wb_scan_one, dim3(1), dim3(kOneWaves * kWave), 0, st, cnt, G, start);
+  } else {
+    hipLaunchKernelGGL(k_wb_block_sums, dim3(static_cast<unsigned>(nb)), dim3(kScanThreads), 0,
+                       st, cnt, G, bsum);
+    hipLaunchKernelGGL(k_wb_scan_sums, dim3(1), dim3(1024), 0, st, bsum, nb);
+    hipLaunchKernelGGL(k_wb_block_scan, dim3(static_cast<unsigned>(nb)), dim3(kScanThreads), 0,
+                       st, cnt, G, bsum, start);
+  }
   if (n > 0)
     hipLaunchKernelGGL(k_wb_place, dim3(static_cast<unsigned>(ceil_div(n, kIndexThreads))),
-                       dim3(kIndexThreads), 0, st, indices, n, G, start, cnt, list);
+                       dim3(kIndexThreads), 0, st, indices, n, G, start, cnt, list, one);
   hipLaunchKernelGGL(k_whiteboard_rows, dim3(static_cast<unsigned>(ceil_div(G, kRowWaves))),
-                     dim3(kRowWaves * kWave), 0, st, src, coeff, start, list, G, H, wb);
+                     dim3(kRowWaves * kWave), 0, st, src, coeff, start, list, one, G, H, wb);
   return hipGetLastError();
 }
 

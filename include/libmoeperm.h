@@ -110,6 +110,27 @@ moe_status_t moe_permute(const void* x, const int32_t* expert_ids, const uint8_t
                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * moe_permute_rows -- the row move of the permute alone, for a routing that
+ * is already resolved.
+ *
+ * [EP] _permute (x gathered by precomputed permuted_indices): every token's
+ * row is copied to the rows its slots own,
+ *     permuted[row_of_slot[t*K + k]] = x[t]   for row_of_slot[t*K + k] in [0, N),
+ * e.g. a second [T, H] tensor moved with the routing of an earlier
+ * moe_permute call. Rows that no slot names are left as they are; slots
+ * outside [0, N) are skipped.
+ *
+ *  x            bf16 [T, H]    in
+ *  row_of_slot  int32 [T, K]   in  (moe_permute's output)
+ *  permuted     bf16 [N, H]    out
+ * Errors: INVALID_ARG for T < 0, K outside [1,16], T*K > INT32_MAX, H <= 0, N
+ * outside [0, INT32_MAX], a required pointer NULL or misaligned; UNSUPPORTED
+ * for H % 8 != 0.
+ * ------------------------------------------------------------------------ */
+moe_status_t moe_permute_rows(const void* x, const int32_t* row_of_slot, int64_t T, int32_t H,
+                              int32_t K, int64_t N, void* permuted, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * moe_permute_noalloc -- moe_permute without a workspace argument, for
  * callers that cannot allocate device memory: code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc.

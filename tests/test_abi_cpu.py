@@ -134,6 +134,20 @@ def test_permute_table_fits_the_noalloc_array(lib):
 
 
 @no_gpu
+def test_permute_rows_checks(lib):
+    f = lambda x=P, ros=P, T=16, H=64, K=2, N=32, out=P: lib.moe_permute_rows(x, ros, T, H, K, N,
+                                                                             out, None)
+    assert f(T=-1) == INVALID
+    assert f(K=0) == INVALID
+    assert f(K=17) == INVALID
+    assert f(H=12) == UNSUPPORTED
+    assert f(N=-1) == INVALID
+    assert f(x=P + 8) == INVALID
+    assert f(ros=None) == INVALID
+    assert f(out=None) == INVALID
+
+
+@no_gpu
 def test_permute_noalloc_checks(lib):
     # size checks come first, before any device lookup
     f = lambda T=16, K=2, E=4: lib.moe_permute_noalloc(P, P, None, 0, T, 64, K, E, P, P, P, P, P,

@@ -89,3 +89,25 @@ def test_permute_config5_routing(moe_lib):
     got, ref = _run_and_compare(moe_lib, np.zeros((g["cfg"]["T"], 8), np.uint16),
                                 g["expert_ids"], g["cfg"]["E"], rows=False)
     assert int((ref["expert_counts"] == 0).sum()) == g["cfg"]["empty_experts"]
+
+
+@pytest.mark.parametrize("T,K,E,H,special,seed", [
+    (300, 2, 8, 128, 0, 21), (1100, 6, 64, 2056, 3, 22), (40, 16, 40, 32, 0, 23),
+])
+def test_permute_rows_applies_a_routing(moe_lib, T, K, E, H, special, seed):
+    """moe_permute_rows moves a second tensor with the oracle's routing: its
+    rows equal the oracle permute of that tensor; rows no slot names keep
+    their contents."""
+    rng = np.random.default_rng(seed)
+    ids = np.argsort(rng.random((T, E + special)), axis=1)[:, :K].astype(np.int32)
+    x2 = W.normal_bf16(rng, (T, H))
+    ref = oracle.permute(x2, ids, E)
+    N = T * K
+    n = int(ref["expert_offsets"][-1])
+    print(f"permute_rows T={T} K={K} E={E} H={H} rows={n}", flush=True)
+    out = torch.full((N, H), 3.0, dtype=torch.bfloat16, device="cuda")
+    moe_lib.moe_permute_rows(to_dev_bf16(x2), to_dev(ref["row_of_slot"]), T, H, K, N, out)
+    torch.cuda.synchronize()
+    got = bits(out)
+    np.testing.assert_array_equal(got[:n], ref["permuted"][:n])
+    assert (got[n:] == W.bf16_from_f32(np.float32([3.0]))[0]).all()

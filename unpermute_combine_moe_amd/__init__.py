@@ -11,7 +11,7 @@ from .binding import (  # noqa: F401
     EXPORTS, LIB_PATH, MoeError, MoeSpecialExperts, combine_alloc, combine_grad_alloc,
     grouped_gemm_alloc, load,
     make_special, moe_grouped_gemm_swiglu, moe_grouped_gemm_swiglu_workspace_size, moe_permute,
-    moe_permute_noalloc, moe_permute_workspace_size, moe_rank_to_expert_reorder,
+    moe_permute_noalloc, moe_permute_rows, moe_permute_workspace_size, moe_rank_to_expert_reorder,
     moe_rank_to_expert_reorder_workspace_size, moe_unpermute_combine, moe_unpermute_grad,
     moe_unpermute_combine_grad, moe_unpermute_combine_grad_workspace_size,
     moe_deredundency_dispatch_indices, moe_deredundency_dispatch_indices_workspace_size,

@@ -43,7 +43,7 @@ class MoeSpecialExperts(ctypes.Structure):
 
 EXPORTS = (
     "moe_status_str", "moe_abi_version",
-    "moe_permute_workspace_size", "moe_permute", "moe_permute_noalloc",
+    "moe_permute_workspace_size", "moe_permute", "moe_permute_noalloc", "moe_permute_rows",
     "moe_rank_to_expert_reorder_workspace_size", "moe_rank_to_expert_reorder",
     "moe_grouped_gemm_swiglu_workspace_size", "moe_grouped_gemm_swiglu",
     "moe_unpermute_combine", "moe_unpermute_grad", "moe_permute_grad",
@@ -73,6 +73,7 @@ def load(path: str = LIB_PATH):
     lib.moe_permute_workspace_size.argtypes = [_i64, _i32, _i32, sz]
     lib.moe_permute.argtypes = [_vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp,
                                 _vp, _vp, ctypes.c_size_t, _vp]
+    lib.moe_permute_rows.argtypes = [_vp, _vp, _i64, _i32, _i32, _i64, _vp, _vp]
     lib.moe_permute_noalloc.argtypes = [_vp, _vp, _vp, _i32, _i64, _i32, _i32, _i32, _vp, _vp,
                                         _vp, _vp, _vp, _vp]
     lib.moe_rank_to_expert_reorder_workspace_size.argtypes = [_i32, _i32, sz]
@@ -202,6 +203,13 @@ def moe_permute(x, expert_ids, T, H, K, num_experts, permuted, sorted_slot, row_
         _ptr(row_of_slot, _I32, "row_of_slot"), _ptr(expert_counts, _I32, "expert_counts"),
         _ptr(expert_offsets, _I32, "expert_offsets"), _ptr(ws, None, "workspace"),
         ws.numel() if ws is not None else 0, _stream(stream)), "moe_permute")
+
+
+def moe_permute_rows(x, row_of_slot, T, H, K, N, permuted, stream=None):
+    """The permute's row move alone: permuted[row_of_slot[t, k]] = x[t]."""
+    _check(load().moe_permute_rows(
+        _ptr(x, _BF16, "x"), _ptr(row_of_slot, _I32, "row_of_slot"), T, H, K, N,
+        _ptr(permuted, _BF16, "permuted"), _stream(stream)), "moe_permute_rows")
 
 
 def moe_permute_noalloc(x, expert_ids, T, H, K, num_experts, permuted, sorted_slot, row_of_slot,

@@ -122,6 +122,18 @@ MOE_API moe_status_t moe_permute(const void* x, const int32_t* expert_ids,
                                         workspace, stream));
 }
 
+MOE_API moe_status_t moe_permute_rows(const void* x, const int32_t* row_of_slot, int64_t T,
+                                      int32_t H, int32_t K, int64_t N, void* permuted,
+                                      hipStream_t stream) {
+  if (moe_status_t s = check_tk(T, K)) return s;
+  if (moe_status_t s = check_h(H)) return s;
+  if (N < 0 || N > INT32_MAX) return MOE_ERR_INVALID_ARG;
+  if (T > 0 && (!row_ok(x) || !word_ok(row_of_slot))) return MOE_ERR_INVALID_ARG;
+  if (N > 0 && !row_ok(permuted)) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_permute_rows(u16(x), row_of_slot, T, H, K, N, u16(permuted),
+                                             stream));
+}
+
 // --------------------------------------------------------------------------- reorder
 
 MOE_API moe_status_t moe_rank_to_expert_reorder_workspace_size(int32_t R, int32_t E_local,

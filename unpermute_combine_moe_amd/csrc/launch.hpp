@@ -29,6 +29,9 @@ hipError_t launch_permute(const uint16_t* x, const int32_t* ids, SlotMask mk, in
                           uint16_t* permuted, int32_t* sorted_slot, int32_t* row_of_slot,
                           int32_t* counts, int32_t* offsets, void* ws, hipStream_t st);
 
+hipError_t launch_permute_rows(const uint16_t* x, const int32_t* row_of_slot, int64_t T, int H,
+                               int K, int64_t N, uint16_t* permuted, hipStream_t st);
+
 size_t reorder_workspace_bytes(int R, int E_local);
 hipError_t launch_reorder(const uint16_t* x, const int32_t* counts, int R, int E_local, int64_t N,
                           int H, uint16_t* y, int32_t* perm, int32_t* inv_perm,

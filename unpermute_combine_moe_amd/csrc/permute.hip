@@ -8,12 +8,15 @@
 //
 // Layout of the work: the T*K slots are cut into chunks of kChunkWaves waves x
 // 64 lanes x `iters` slots; wave w of a chunk owns a contiguous run of
-// 64*iters slots, so "earlier wave" means "earlier slots". Counts are kept per
-// (expert, chunk); a chunk's first row inside bucket e is the offset of e plus
-// the counts of e in earlier chunks. The chunk size keeps the count table
-// small, so every scatter workgroup derives these from the whole table itself
-// (two launches before the row copy). No global atomics: rank assignment is
-// deterministic.
+// 64*iters slots, so "earlier wave" means "earlier slots". Three launches:
+//  1. per chunk: its (chunk, expert) count table row and every slot's rank
+//     among the chunk's slots with its id (a wave-level match);
+//  2. one workgroup scans the table: expert counts and offsets, and for every
+//     chunk its first row in each bucket (offsets[e] plus the counts of e in
+//     earlier chunks);
+//  3. per token: each slot's row (that first row plus its rank in the chunk),
+//     both index maps, and the row copy.
+// No global atomics: rank assignment is deterministic.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -22,6 +25,8 @@ namespace {
 
 constexpr int kChunkWaves = 4;
 constexpr int kChunkThreads = kChunkWaves * kWave;
+constexpr int kMaxExpertsPermute = 1024;
+constexpr int kMaxTopK = 16;
 
 struct PermutePlan {
   int iters;    // slots per lane per chunk
@@ -29,27 +34,14 @@ struct PermutePlan {
   int64_t nblk; // number of chunks
 };
 
-// Threads that share one expert's walk of the count table: a power of two,
-// at most a wave, with threads-per-expert x E within the workgroup.
-__host__ __device__ inline int walk_threads(int E) {
-  int t = 1;
-  while (t < kWave && 2 * t * E <= kChunkThreads) t *= 2;
-  return t;
-}
-
 // Chunks are sized so the (chunk, expert) count table holds at most
-// kTableMax entries (every scatter workgroup reads all of it), with at least
-// 8 / walk_threads(E) (and at least 2) slots per lane: more, smaller chunks
-// lengthen the table walk, which walk_threads(E) threads per expert share,
-// and shorten the counting and the scatter.
+// kTableMax entries (one workgroup scans it), with at least two slots per lane.
 constexpr int64_t kTableMax = 16384;
 
 PermutePlan plan_for(int64_t S, int E) {
   PermutePlan p;
   const int64_t target = std::max<int64_t>(1, std::min<int64_t>(256, kTableMax / E));
-  const int min_iters = std::max(2, 8 / walk_threads(E));
-  p.iters = static_cast<int>(
-      std::max<int64_t>(min_iters, ceil_div(S, int64_t(kChunkThreads) * target)));
+  p.iters = static_cast<int>(std::max<int64_t>(2, ceil_div(S, int64_t(kChunkThreads) * target)));
   p.chunk = int64_t(kChunkThreads) * p.iters;
   p.nblk = ceil_div(S, p.chunk);
   return p;
@@ -70,43 +62,20 @@ __device__ __forceinline__ uint64_t match_key(int key, int nbits) {
 // independent, so a batch costs one memory latency instead of kBatch.
 constexpr int kBatch = 8;
 
-// Per-chunk histogram, chunk-major: hist[b * E + e] = #slots of chunk b with id e.
+// Pass 1 over a chunk: its histogram, chunk-major (table[b * E + e] = #slots of
+// chunk b with id e), and every slot's rank inside the chunk among the slots
+// with its id, stored in row_of_slot (-1 for slots without a row); the row
+// kernel turns it into the row. Wave w of the chunk owns a contiguous run of
+// slots; lanes holding the same id are found with a ballot per id bit (a
+// wave-level match), ranked with mbcnt, and the group's lowest lane advances
+// the wave's running count in LDS -- deterministic, no global atomics.
 __global__ void __launch_bounds__(kChunkThreads)
-k_route_count(const int32_t* __restrict__ ids, SlotMask mk, int64_t S, int E, int iters,
-              int32_t* __restrict__ hist) {
-  extern __shared__ int32_t cnt[];  // [E]
-  for (int e = threadIdx.x; e < E; e += kChunkThreads) cnt[e] = 0;
-  __syncthreads();
-  const int64_t b = blockIdx.x;
-  const int64_t base = b * int64_t(kChunkThreads) * iters;
-  for (int j0 = 0; j0 < iters; j0 += kBatch) {
-    int id[kBatch];
-    bool act[kBatch];
-#pragma unroll
-    for (int q = 0; q < kBatch; ++q) {
-      const int64_t s = base + int64_t(j0 + q) * kChunkThreads + threadIdx.x;
-      const bool in = j0 + q < iters && s < S;
-      id[q] = in ? ids[s] : -1;
-      act[q] = in && mk.active(s);
-    }
-#pragma unroll
-    for (int q = 0; q < kBatch; ++q)
-      if (act[q] && id[q] >= 0 && id[q] < E) atomicAdd(&cnt[id[q]], 1);
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kChunkThreads) hist[b * E + e] = cnt[e];
-}
-
-// Stable scatter of the slots of chunk b, given chunk_base(e) = the first row
-// of bucket e that belongs to this chunk: writes row_of_slot[s] and
-// sorted_slot[row], and -1 into sorted_slot rows [N, S) of the chunk's range.
-template <typename ChunkBase>
-__device__ void scatter_chunk(const int32_t* __restrict__ ids, SlotMask mk, int64_t S, int E,
-                              int iters,
-                              int64_t b, ChunkBase chunk_base, int32_t N, int32_t* run,
-                              int32_t* __restrict__ sorted_slot, int32_t* __restrict__ row_of_slot) {
+k_route_rank(const int32_t* __restrict__ ids, SlotMask mk, int64_t S, int E, int iters,
+             int32_t* __restrict__ table, int32_t* __restrict__ row_of_slot) {
+  extern __shared__ int32_t run[];  // [kChunkWaves * E]
   const int w = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
+  const int64_t b = blockIdx.x;
   for (int i = threadIdx.x; i < kChunkWaves * E; i += kChunkThreads) run[i] = 0;
   __syncthreads();
   const int64_t wbase = b * int64_t(kChunkThreads) * iters + int64_t(w) * kWave * iters;
@@ -125,8 +94,14 @@ __device__ void scatter_chunk(const int32_t* __restrict__ ids, SlotMask mk, int6
 #pragma unroll
     for (int q = 0; q < kBatch; ++q) id[q] = act[q] ? id[q] : -1;
   };
-  // pass 1: per-wave counts
-  for (int j0 = 0; j0 < iters; j0 += kBatch) {
+  // per-wave counts (the first batch of ids is kept for the ranking pass,
+  // which then needs no second load when a lane has at most kBatch slots)
+  int id0[kBatch];
+  load_batch(0, id0);
+#pragma unroll
+  for (int q = 0; q < kBatch; ++q)
+    if (id0[q] >= 0 && id0[q] < E) atomicAdd(&my[id0[q]], 1);
+  for (int j0 = kBatch; j0 < iters; j0 += kBatch) {
     int id[kBatch];
     load_batch(j0, id);
 #pragma unroll
@@ -134,23 +109,29 @@ __device__ void scatter_chunk(const int32_t* __restrict__ ids, SlotMask mk, int6
       if (id[q] >= 0 && id[q] < E) atomicAdd(&my[id[q]], 1);
   }
   __syncthreads();
-  // first row of every (wave, expert): chunk base plus the counts of earlier waves
+  // the chunk's histogram, and the first rank of every (wave, expert) inside
+  // the chunk: the counts of the earlier waves
   for (int e = threadIdx.x; e < E; e += kChunkThreads) {
-    int32_t r = chunk_base(e);
+    int32_t r = 0;
 #pragma unroll
     for (int ww = 0; ww < kChunkWaves; ++ww) {
       const int32_t c = run[ww * E + e];
       run[ww * E + e] = r;
       r += c;
     }
+    table[b * E + e] = r;
   }
   __syncthreads();
-  // pass 2: each wave walks its slots in order; lanes with equal ids are ranked
-  // by lane index, and the group's lowest lane advances the running row.
+  // each wave walks its slots in order
   const int nbits = 32 - __builtin_clz(static_cast<unsigned>(E));  // keys 0..E fit
   for (int j0 = 0; j0 < iters; j0 += kBatch) {
     int id[kBatch];
-    load_batch(j0, id);
+    if (j0 == 0) {
+#pragma unroll
+      for (int q = 0; q < kBatch; ++q) id[q] = id0[q];
+    } else {
+      load_batch(j0, id);
+    }
 #pragma unroll
     for (int q = 0; q < kBatch; ++q) {
       if (j0 + q >= iters) break;
@@ -159,96 +140,94 @@ __device__ void scatter_chunk(const int32_t* __restrict__ ids, SlotMask mk, int6
       const int key = real ? id[q] : E;
       const uint64_t same = match_key(key, nbits);
       const int rank = rank_below(same);
-      int32_t row = -1;
-      if (real) row = my[id[q]] + rank;
+      int32_t local = -1;
+      if (real) local = my[id[q]] + rank;
       if (real && rank == 0) my[id[q]] += __popcll(same);
-      if (s < S) {
-        row_of_slot[s] = row;
-        if (real) sorted_slot[row] = static_cast<int32_t>(s);
-      }
+      if (s < S) row_of_slot[s] = local;
     }
   }
-  // rows past N (no slot maps there) read -1
-  const int64_t r_lo = b * int64_t(kChunkThreads) * iters;
-  const int64_t r_hi = std::min<int64_t>(S, r_lo + int64_t(kChunkThreads) * iters);
-  for (int64_t r = r_lo + threadIdx.x; r < r_hi; r += kChunkThreads)
-    if (r >= N) sorted_slot[r] = -1;
 }
 
-// Scan and scatter in one launch: every workgroup sums the chunk-major count
-// table itself (per expert: all chunks, and the chunks before its own), scans
-// the expert totals in LDS, and chunk 0 publishes counts and offsets.
-__global__ void __launch_bounds__(kChunkThreads)
-k_route_scan_scatter(const int32_t* __restrict__ ids, SlotMask mk, int64_t S, int E, int iters,
-                     int64_t nblk,
-                     const int32_t* __restrict__ hist, int32_t* __restrict__ counts,
-                     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_slot,
-                     int32_t* __restrict__ row_of_slot) {
-  extern __shared__ int32_t sm[];  // run[kChunkWaves * E] | before[E] | off[E] | part[kChunkThreads]
-  int32_t* run = sm;
-  int32_t* before = sm + kChunkWaves * E;
-  int32_t* off = before + E;
-  int32_t* part = off + E;
-  const int64_t b = blockIdx.x;
+// Pass 2, one workgroup: per expert, the exclusive prefix of its column of the
+// count table (the rows of that expert in earlier chunks), the expert totals
+// and their exclusive scan (counts, offsets); the table is overwritten with
+// every chunk's first row per expert, offsets[e] + the earlier chunks' rows.
+constexpr int kScanThreads = 1024;
+__host__ __device__ inline int scan_threads_per_expert(int E) {
+  int t = 1;
+  while (t < kWave && 2 * t * E <= kScanThreads) t *= 2;
+  return t;
+}
+
+// A column range of one thread holds at most this many chunks: nblk <=
+// kTableMax / E chunks are shared by t = scan_threads_per_expert(E) threads with
+// t * E > 512 (the loop stops at the first t with 2 t E > 1024), or t = 64 for
+// E <= 8 (at most 256 chunks).
+constexpr int kScanRange = 32;
+
+__global__ void __launch_bounds__(kScanThreads)
+k_route_scan(int E, int64_t nblk, int32_t* __restrict__ table, int32_t* __restrict__ counts,
+             int32_t* __restrict__ offsets) {
+  __shared__ int32_t tot[kMaxExpertsPermute];
   // tpe consecutive threads (an aligned group inside one wave) share expert
-  // e's walk, each taking every tpe-th chunk; their sums meet by xor shuffles
-  const int tpe = walk_threads(E);
-  for (int g = threadIdx.x; g < E * tpe; g += kChunkThreads) {
-    const int e = g / tpe, sub = g % tpe;
-    int32_t tot = 0, pre = 0;
-    for (int64_t b0 = sub; b0 < nblk; b0 += int64_t(kBatch) * tpe) {
-      int32_t c[kBatch];
+  // e's column, thread sub taking the contiguous chunk range [lo, hi), all of
+  // whose entries it loads at once and keeps for the write-back
+  const int tpe = scan_threads_per_expert(E);
+  const int len = static_cast<int>(ceil_div(nblk, tpe));
+  const int g = threadIdx.x;
+  const int e = g / tpe, sub = g % tpe;
+  const bool mine = e < E;
+  // table indices fit 32 bits: nblk * E <= kTableMax
+  const int lo = static_cast<int>(std::min<int64_t>(nblk, int64_t(sub) * len));
+  const int hi = static_cast<int>(std::min<int64_t>(nblk, int64_t(lo) + len));
+  int32_t c[kScanRange];
 #pragma unroll
-      for (int q = 0; q < kBatch; ++q) {
-        const int64_t bq = b0 + int64_t(q) * tpe;
-        c[q] = (bq < nblk) ? hist[bq * E + e] : 0;
-      }
-#pragma unroll
-      for (int q = 0; q < kBatch; ++q) {
-        tot += c[q];
-        pre += (b0 + int64_t(q) * tpe < b) ? c[q] : 0;
-      }
-    }
-    for (int o = tpe / 2; o > 0; o >>= 1) {
-      tot += __shfl_xor(tot, o, kWave);
-      pre += __shfl_xor(pre, o, kWave);
-    }
-    if (sub == 0) {
-      off[e] = tot;
-      before[e] = pre;
-    }
-  }
-  __syncthreads();
-  // exclusive scan of the expert totals: each thread a contiguous run of experts
-  const int per = (E + kChunkThreads - 1) / kChunkThreads;
-  const int lo = std::min(E, static_cast<int>(threadIdx.x) * per);
-  const int hi = std::min(E, lo + per);
+  for (int q = 0; q < kScanRange; ++q) c[q] = (mine && lo + q < hi) ? table[(lo + q) * E + e] : 0;
   int32_t sum = 0;
-  for (int e = lo; e < hi; ++e) sum += off[e];
-  part[threadIdx.x] = sum;
-  __syncthreads();
-  for (int o = 1; o < kChunkThreads; o <<= 1) {
-    const int32_t v = threadIdx.x >= o ? part[threadIdx.x - o] : 0;
-    __syncthreads();
-    part[threadIdx.x] += v;
-    __syncthreads();
+#pragma unroll
+  for (int q = 0; q < kScanRange; ++q) sum += c[q];
+  // inclusive prefix of the range sums inside the group, and the expert total
+  int32_t incl = sum;
+  for (int o = 1; o < tpe; o <<= 1) {
+    const int32_t v = __shfl_up(incl, o, kWave);
+    if (sub >= o) incl += v;
   }
-  int32_t acc = part[threadIdx.x] - sum;
-  const int32_t N = part[kChunkThreads - 1];
-  for (int e = lo; e < hi; ++e) {
-    const int32_t c = off[e];
-    off[e] = acc;
-    if (b == 0) {
-      counts[e] = c;
-      offsets[e] = acc;
+  const int32_t total = __shfl(incl, (threadIdx.x % kWave) | (tpe - 1), kWave);
+  if (mine && sub == 0) tot[e] = total;
+  __syncthreads();
+  // exclusive scan of the expert totals by the first wave: each lane a run of
+  // ceil(E / 64) experts, then a wave prefix of the run sums
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    const int per = (E + kWave - 1) / kWave;
+    const int elo = std::min(E, lane * per), ehi = std::min(E, elo + per);
+    int32_t run = 0;
+    for (int x = elo; x < ehi; ++x) run += tot[x];
+    int32_t pre = run;
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int32_t v = __shfl_up(pre, o, kWave);
+      if (lane >= o) pre += v;
     }
-    acc += c;
+    int32_t acc = pre - run;
+    for (int x = elo; x < ehi; ++x) {
+      const int32_t cx = tot[x];
+      counts[x] = cx;
+      offsets[x] = acc;
+      tot[x] = acc;  // now the expert's first row
+      acc += cx;
+    }
+    if (lane == kWave - 1) offsets[E] = pre;
   }
-  if (b == 0 && threadIdx.x == 0) offsets[E] = N;
   __syncthreads();
-  scatter_chunk(
-      ids, mk, S, E, iters, b, [&](int e) { return off[e] + before[e]; }, N, run, sorted_slot,
-      row_of_slot);
+  // every chunk's first row per expert
+  if (mine) {
+    int32_t r = tot[e] + incl - sum;
+#pragma unroll
+    for (int q = 0; q < kScanRange; ++q) {
+      if (lo + q < hi) table[(lo + q) * E + e] = r;
+      r += c[q];
+    }
+  }
 }
 
 __global__ void __launch_bounds__(kChunkThreads)
@@ -259,47 +238,137 @@ k_route_empty(int E, int32_t* __restrict__ counts, int32_t* __restrict__ offsets
   }
 }
 
-// Row copy, token-major: each wave reads its token's row once and writes it to
-// the K rows the token's slots landed on (16-byte vectors, coalesced).
+// Pass 3, token-major: the rows of a token's slots (the chunk's first row for
+// the slot's expert plus the slot's rank inside the chunk), both index maps,
+// -1 for the rows past N, and the row copy: each wave reads its token's row
+// once and writes it to the K rows its slots landed on (16-byte vectors,
+// coalesced). The slots of the workgroup's tokens are resolved first, one
+// thread each, and their rows shared through LDS.
 constexpr int kRowWaves = 4;
 constexpr int kRowBatch = 4;  // 16-byte chunks per lane loaded before their stores
 __global__ void __launch_bounds__(kRowWaves * kWave)
-k_permute_rows(const uint16_t* __restrict__ x, const int32_t* __restrict__ row_of_slot,
-               int64_t T, int H, int K, int64_t S, uint16_t* __restrict__ permuted, int nsplit) {
-  // nsplit waves share a token, each taking every nsplit-th 64-chunk row of it
+k_permute_rows(const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, SlotMask mk,
+               int64_t T, int H, int K, int E, int64_t chunk, const int32_t* __restrict__ table,
+               const int32_t* __restrict__ offsets, int32_t* __restrict__ row_of_slot,
+               int32_t* __restrict__ sorted_slot, uint16_t* __restrict__ permuted, int nsplit) {
+  __shared__ int32_t s_rows[kRowWaves * kMaxTopK];
+  const int tokens = kRowWaves / nsplit;  // tokens of this workgroup
+  const int64_t t0 = int64_t(blockIdx.x) * tokens;
+  const int64_t S = T * K;
+  // this wave's token and its share of the row; the first batch of the row's
+  // loads goes out before the slots are resolved (it does not depend on them)
   const int w = threadIdx.x / kWave;
   const int part = w % nsplit;
-  const int64_t t = uniform(static_cast<int>(blockIdx.x * (kRowWaves / nsplit) + w / nsplit));
-  if (t >= T) return;
+  const int lt = w / nsplit;
+  const int64_t t = t0 + lt;
   const int lane = threadIdx.x % kWave;
-  int32_t rows[16];
-#pragma unroll
-  for (int k = 0; k < 16; ++k) rows[k] = (k < K) ? row_of_slot[t * K + k] : -1;
   const int chunks = H / 8;
   const uint16_t* src = x + t * H;
+  const int step = kWave * nsplit;
+  const bool copy = permuted != nullptr && t < T;
+  Vec8 v0[kRowBatch];
+  if (copy) {
+#pragma unroll
+    for (int bb = 0; bb < kRowBatch; ++bb) {
+      const int c = lane + part * kWave + bb * step;
+      if (c < chunks) v0[bb] = load16_nt(src + c * 8);
+    }
+  }
+  const int32_t N = offsets[E];
+  // one thread per slot of the workgroup's tokens
+  if (static_cast<int>(threadIdx.x) < tokens * K) {
+    const int64_t s = t0 * K + threadIdx.x;
+    int32_t row = -1;
+    if (s < S) {
+      const int32_t id = ids[s];
+      const int32_t local = row_of_slot[s];
+      if (local >= 0 && id >= 0 && id < E && mk.active(s)) {
+        row = table[(s / chunk) * E + id] + local;
+        sorted_slot[row] = static_cast<int32_t>(s);
+      }
+      row_of_slot[s] = row;
+      if (s >= N) sorted_slot[s] = -1;  // rows past N (one slot per row)
+    }
+    s_rows[threadIdx.x] = row;
+  }
+  __syncthreads();
+  if (!copy) return;
+  // nsplit waves share a token, each taking every nsplit-th 64-chunk row of it
+  int32_t rows[kMaxTopK];
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k) rows[k] = (k < K) ? s_rows[lt * K + k] : -1;
   // kRowBatch chunks per lane: all loads issued before their stores
+  for (int c0 = lane + part * kWave; c0 < chunks; c0 += step * kRowBatch) {
+    Vec8 v[kRowBatch];
+    if (c0 == lane + part * kWave) {
+#pragma unroll
+      for (int bb = 0; bb < kRowBatch; ++bb) v[bb] = v0[bb];
+    } else {
+#pragma unroll
+      for (int bb = 0; bb < kRowBatch; ++bb) {
+        const int c = c0 + bb * step;
+        if (c < chunks) v[bb] = load16_nt(src + c * 8);
+      }
+    }
+#pragma unroll
+    for (int bb = 0; bb < kRowBatch; ++bb) {
+      const int c = c0 + bb * step;
+      if (c >= chunks) continue;
+#pragma unroll
+      for (int k = 0; k < kMaxTopK; ++k) {
+        if (k < K && rows[k] >= 0 && rows[k] < S)
+          store16(permuted + int64_t(rows[k]) * H + c * 8, v[bb]);
+      }
+    }
+  }
+}
+
+// A routing already resolved (row_of_slot) applied to a token tensor, token-major:
+// each wave reads its token's row once and writes it to the rows of its slots.
+__global__ void __launch_bounds__(kRowWaves * kWave)
+k_apply_rows(const uint16_t* __restrict__ x, const int32_t* __restrict__ row_of_slot, int64_t T,
+             int H, int K, int64_t N, uint16_t* __restrict__ permuted, int nsplit) {
+  const int w = threadIdx.x / kWave;
+  const int part = w % nsplit;
+  const int64_t t = int64_t(blockIdx.x) * (kRowWaves / nsplit) + w / nsplit;
+  if (t >= T) return;
+  const int lane = threadIdx.x % kWave;
+  int32_t rows[kMaxTopK];
+#pragma unroll
+  for (int k = 0; k < kMaxTopK; ++k) rows[k] = (k < K) ? row_of_slot[t * K + k] : -1;
+  const int chunks = H / 8;
+  const uint16_t* src = x + t * H;
   const int step = kWave * nsplit;
   for (int c0 = lane + part * kWave; c0 < chunks; c0 += step * kRowBatch) {
     Vec8 v[kRowBatch];
 #pragma unroll
-    for (int b = 0; b < kRowBatch; ++b) {
-      const int c = c0 + b * step;
-      if (c < chunks) v[b] = load16_nt(src + c * 8);
+    for (int bb = 0; bb < kRowBatch; ++bb) {
+      const int c = c0 + bb * step;
+      if (c < chunks) v[bb] = load16_nt(src + c * 8);
     }
 #pragma unroll
-    for (int b = 0; b < kRowBatch; ++b) {
-      const int c = c0 + b * step;
+    for (int bb = 0; bb < kRowBatch; ++bb) {
+      const int c = c0 + bb * step;
       if (c >= chunks) continue;
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        if (k < K && rows[k] >= 0 && rows[k] < S)
-          store16(permuted + int64_t(rows[k]) * H + c * 8, v[b]);
+      for (int k = 0; k < kMaxTopK; ++k) {
+        if (k < K && rows[k] >= 0 && rows[k] < N)
+          store16(permuted + int64_t(rows[k]) * H + c * 8, v[bb]);
       }
     }
   }
 }
 
 }  // namespace
+
+hipError_t launch_permute_rows(const uint16_t* x, const int32_t* row_of_slot, int64_t T, int H,
+                               int K, int64_t N, uint16_t* permuted, hipStream_t st) {
+  if (T == 0) return hipGetLastError();
+  const int nsplit = (H / 8 >= 2 * kWave && T < kSplitBelowTokens) ? 2 : 1;
+  hipLaunchKernelGGL(k_apply_rows, dim3(static_cast<unsigned>(ceil_div(T, kRowWaves / nsplit))),
+                     dim3(kRowWaves * kWave), 0, st, x, row_of_slot, T, H, K, N, permuted, nsplit);
+  return hipGetLastError();
+}
 
 size_t permute_workspace_bytes(int64_t T, int K, int E) {
   const PermutePlan p = plan_for(T * K, E);
@@ -316,20 +385,16 @@ hipError_t launch_permute(const uint16_t* x, const int32_t* ids, SlotMask mk, in
     hipLaunchKernelGGL(k_route_empty, dim3(1), dim3(kChunkThreads), 0, st, E, counts, offsets);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(k_route_count, dim3(static_cast<unsigned>(p.nblk)), dim3(kChunkThreads),
-                     E * sizeof(int32_t), st, ids, mk, S, E, p.iters, table);
-  const size_t lds = (size_t(kChunkWaves) * E + 2 * E + kChunkThreads) * sizeof(int32_t);
-  hipLaunchKernelGGL(k_route_scan_scatter, dim3(static_cast<unsigned>(p.nblk)),
-                     dim3(kChunkThreads), lds, st, ids, mk, S, E, p.iters, p.nblk, table, counts,
-                     offsets, sorted_slot, row_of_slot);
-  if (permuted != nullptr) {
-    // two waves per token when there are too few tokens for several rounds of waves
-    const int nsplit = (H / 8 >= 2 * kWave && T < kSplitBelowTokens) ? 2 : 1;
-    hipLaunchKernelGGL(k_permute_rows,
-                       dim3(static_cast<unsigned>(ceil_div(T, kRowWaves / nsplit))),
-                       dim3(kRowWaves * kWave), 0, st, x, row_of_slot, T, H, K, S, permuted,
-                       nsplit);
-  }
+  hipLaunchKernelGGL(k_route_rank, dim3(static_cast<unsigned>(p.nblk)), dim3(kChunkThreads),
+                     size_t(kChunkWaves) * E * sizeof(int32_t), st, ids, mk, S, E, p.iters, table,
+                     row_of_slot);
+  hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(kScanThreads), 0, st, E, p.nblk, table, counts,
+                     offsets);
+  // two waves per token when there are too few tokens for several rounds of waves
+  const int nsplit = (permuted != nullptr && H / 8 >= 2 * kWave && T < kSplitBelowTokens) ? 2 : 1;
+  hipLaunchKernelGGL(k_permute_rows, dim3(static_cast<unsigned>(ceil_div(T, kRowWaves / nsplit))),
+                     dim3(kRowWaves * kWave), 0, st, x, ids, mk, T, H, K, E, p.chunk, table,
+                     offsets, row_of_slot, sorted_slot, permuted, nsplit);
   return hipGetLastError();
 }
 

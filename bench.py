@@ -117,6 +117,11 @@ def permute_bytes(T, K, H, N):
     return T * K * 4 + T * H * 2 + N * H * 2 + 2 * T * K * 4 + 0
 
 
+def row_move_bytes(T, K, H, N):
+    """x read once, N rows written, the routing read."""
+    return T * H * 2 + N * H * 2 + T * K * 4
+
+
 def combine_bytes(T, K, H, N, extra_rows=0):
     return N * H * 2 + 3 * T * K * 4 + T * H * 2 + extra_rows * H * 2
 
@@ -280,6 +285,32 @@ def run_ops(args, dev, flush):
     import unpermute_combine_moe_amd as moe
 
     ops = []
+    # the tiny full path, T=64 H=128 E=8 K=2 I=64: permute -> grouped SwiGLU GEMM
+    # -> combine; launch-bound (no roofline target), reported per pass
+    g = W.gen_c1()
+    c = g["cfg"]
+    T, H, E, K, I = c["T"], c["H"], c["E"], c["K"], c["I"]
+    x1, ids1, probs1 = dbf(g["x"], dev), dt(g["expert_ids"], dev), dt(g["probs"], dev)
+    wg1, wu1, wd1 = (dbf(g[k], dev) for k in ("w_gate", "w_up", "w_down"))
+    p1 = moe.permute_alloc(x1, ids1, E)
+    ws_p1 = moe.workspace(moe.moe_permute_workspace_size(T, K, E), dev)
+    ws_g1 = moe.workspace(moe.moe_grouped_gemm_swiglu_workspace_size(E, T * K, H, I), dev)
+    h1 = torch.empty((T * K, I), dtype=torch.bfloat16, device=dev)
+    y1 = torch.empty((T * K, H), dtype=torch.bfloat16, device=dev)
+    out1 = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+
+    def f_c1():
+        moe.moe_permute(x1, ids1, T, H, K, E, p1["permuted"], p1["sorted_slot"], p1["row_of_slot"],
+                        p1["expert_counts"], p1["expert_offsets"], ws_p1)
+        moe.moe_grouped_gemm_swiglu(p1["permuted"], p1["expert_offsets"], E, T * K, H, I, wg1, wu1,
+                                    wd1, h1, y1, ws_g1)
+        moe.moe_unpermute_combine(y1, T * K, p1["row_of_slot"], None, ids1, probs1, T, K, H, E,
+                                  None, None, out1)
+    us, usmin = time_op(f_c1, args.op_iters, None, warm=5)
+    e1 = op_entry("full_path_forward", us, usmin, flops=gemm_flops(T * K, H, I))
+    e1["tokens_per_s"] = round(T / (us * 1e-6), 1)
+    ops.append(dict(workload=c["name"], timing="three calls, caches warm", **e1))
+    del x1, p1, h1, y1, out1
     # permute / combine, T=4096 H=2048 E=64 K=6
     g = W.gen_c2()
     c = g["cfg"]
@@ -298,6 +329,11 @@ def run_ops(args, dev, flush):
     ops.append(dict(workload=c["name"], **op_entry("unpermute_combine",
                                                    *time_op(f_comb, args.op_iters, flush),
                                                    nbytes=combine_bytes(T, K, H, N))))
+    # the permute's row move alone (moe_permute_rows with the routing just built)
+    f_rows = lambda: moe.moe_permute_rows(x, p["row_of_slot"], T, H, K, T * K, p["permuted"])
+    ops.append(dict(workload=c["name"], **op_entry("permute_row_move",
+                                                   *time_op(f_rows, args.op_iters, flush),
+                                                   nbytes=row_move_bytes(T, K, H, N))))
     # the same with x_active_mask: a [T, K] slot mask with 10% of the slots off
     m_np = np.random.default_rng(22).random((T, K)) < 0.9
     mask = torch.from_numpy(m_np).to(dev)
@@ -411,6 +447,18 @@ def run_ops(args, dev, flush):
     us, usmin = time_op(lambda: b.copy_(a), 10, None)
     ops.append(dict(workload="d2d_copy_1GiB", **op_entry("torch_copy", us, usmin,
                                                          nbytes=2 * a.numel() * 2)))
+    del a, b
+    # for scale: the vendor GEMM (torch.matmul, hipBLASLt) on dense bf16 matrices
+    # of the skewed layer's two passes, all 65,536 rows as one matrix (no expert
+    # groups, no SwiGLU), weights [k][n] as the grouped call takes them
+    for name, (M, Kd, Nc) in (("dense_gemm_gate_up_reference", (65536, 2048, 1024)),
+                              ("dense_gemm_down_reference", (65536, 512, 2048))):
+        xa = torch.randn(M, Kd, device=dev, dtype=torch.bfloat16)
+        wa = torch.randn(Kd, Nc, device=dev, dtype=torch.bfloat16) * 0.02
+        us, usmin = time_op(lambda: torch.matmul(xa, wa), args.op_iters, None, warm=3)
+        ops.append(dict(workload=f"dense_{M}x{Kd}x{Nc}", **op_entry(name, us, usmin,
+                                                                   flops=2 * M * Kd * Nc)))
+        del xa, wa
     return ops
 
 
@@ -507,14 +555,20 @@ def main():
     # with --no-ops, the in-step times instead (marked as such)
     permute, _, combine, grad = step_calls(d)
     flush = None if args.no_ops else Flusher(dev)
+    import unpermute_combine_moe_amd as moe
+    row_move = lambda: moe.moe_permute_rows(d["x"], d["row_of_slot"], T, H, K, T * K,
+                                            d["permuted"])
     mem_ops = (("permute", permute, 0, permute_bytes(T, K, H, n_rows)),
                ("unpermute_combine", combine, 2, combine_bytes(T, K, H, n_rows)),
-               ("unpermute_grad", grad, 3, grad_bytes(T, K, H, n_rows)))
+               ("unpermute_grad", grad, 3, grad_bytes(T, K, H, n_rows)),
+               ("permute_row_move", row_move, None, row_move_bytes(T, K, H, n_rows)))
     layer_ops = []
     for name, fn, col, nbytes in mem_ops:
         if flush is not None:
             us, usmin = time_op(fn, args.op_iters, flush)
             timing = "alone, cache flushed"
+        elif col is None:
+            continue
         else:
             us, usmin = float(np.median(seg[:, col])), float(np.min(seg[:, col]))
             timing = "in the layer step"

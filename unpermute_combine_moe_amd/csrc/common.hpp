@@ -119,6 +119,38 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __host__ __device__ constexpr int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// ---- staged-operand ring of the GEMM kernels
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// 16-byte direct global -> LDS load: this lane's 16 bytes land at LDS byte
+// address lds_base + 16 * lane. Issued as inline asm so the compiler does not
+// treat it as an LDS write it must wait for before every later LDS read; the
+// kernel orders these loads itself with wait_vmcnt and stage_barrier.
+__device__ __forceinline__ void load_lds16(const void* gptr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds_base), "v"(gptr)
+               : "memory", "m0");
+}
+
+// Workgroup barrier without a memory fence (a fence would also wait for the
+// loads still in flight); the "memory" clobber keeps the compiler from moving
+// LDS accesses across it.
+__device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Wait until this wave's own LDS accesses have completed.
+__device__ __forceinline__ void wait_lds_reads() {
+  // lgkmcnt(0); vmcnt (63) and expcnt (7) unconstrained
+  __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
+}
+
 // Exclusive scan of in[0..L) into out[0..L) by one workgroup of kThreads
 // threads (each a contiguous run, then a Hillis-Steele scan of the run sums in
 // part[kThreads], shared); returns the total to every thread. in and out may

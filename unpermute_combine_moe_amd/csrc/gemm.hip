@@ -149,36 +149,6 @@ __device__ __forceinline__ int stage_chunk(int row, int chunk) {
   static_assert(kRowBytes == 256 || kRowBytes == 128, "staged row sizes");
 }
 
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt_hi[15:14]).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
-}
-
-// 16-byte direct global -> LDS load: this lane's 16 bytes land at LDS byte
-// address lds_base + 16 * lane. Issued as inline asm so the compiler does not
-// treat it as an LDS write it must wait for before every later LDS read; the
-// kernel orders these loads itself with wait_vmcnt and stage_barrier.
-__device__ __forceinline__ void load_lds16(const void* gptr, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :
-               : "s"(lds_base), "v"(gptr)
-               : "memory", "m0");
-}
-
-// Workgroup barrier without a memory fence (a fence would also wait for the
-// loads still in flight); the "memory" clobber keeps the compiler from moving
-// LDS accesses across it.
-__device__ __forceinline__ void stage_barrier() { asm volatile("s_barrier" ::: "memory"); }
-
-// Wait until this wave's own LDS accesses have completed.
-__device__ __forceinline__ void wait_lds_reads() {
-  // lgkmcnt(0); vmcnt (63) and expcnt (7) unconstrained
-  __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));
-}
-
 __device__ __forceinline__ int swz_b(int k, int c) { return k * (BN / 8) + (c ^ (4 * (k & 3))); }
 
 __device__ __forceinline__ bf16x8_t lds_read_a(const lds_u8_t* base, int slot) {
@@ -581,6 +551,8 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
   }
 }
 
+}  // namespace
+
 int persistent_grid() {
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) == hipSuccess) {
@@ -590,8 +562,6 @@ int persistent_grid() {
   }
   return std::max(kXcds, (cus / kXcds) * kXcds);
 }
-
-}  // namespace
 
 // ws layout: tile_prefix[E+1] | offs[E+1] (int32)
 size_t gemm_workspace_bytes(int E, int64_t /*N_cap*/, int /*H*/, int /*I*/) {

@@ -45,6 +45,7 @@ constexpr int kLoads = kTileChunks / kThreads;        // per thread per operand 
 constexpr int kTileBytes = kTileChunks * 16;
 constexpr int kStageBytes = 2 * kTileBytes;
 constexpr int kSchedThreads = 1024;
+constexpr int kXcds = 8;
 
 // [row][k] tile: row r, 16-byte k-chunk kc (8 per row)
 __device__ __forceinline__ int swz_rk(int r, int kc) { return r * (TK / 8) + (kc ^ ((r >> 1) & 7)); }
@@ -183,9 +184,17 @@ k_bgemm_rows(const uint16_t* __restrict__ A, int K, const uint16_t* __restrict__
   const int32_t* prefix = ws;
   const int32_t* offs = ws + (E + 1);
   const int col_tiles = (Ncols + TN - 1) / TN;
-  const int rt = static_cast<int>(blockIdx.x) / col_tiles;
-  const int ct = static_cast<int>(blockIdx.x) % col_tiles;
-  if (rt >= prefix[E]) return;
+  // Workgroup b runs on XCD b % 8: each XCD takes a contiguous range of the
+  // row-tile-major tile list, so the column tiles of a row block (which share
+  // its A rows) and the row tiles of an expert (which share its weights) meet
+  // in one L2. The grid is a multiple of 8 and covers every real tile.
+  const int total = prefix[E] * col_tiles;
+  const int per_xcd = (total + kXcds - 1) / kXcds;
+  const int pos = static_cast<int>(blockIdx.x) / kXcds;
+  const int tile = (static_cast<int>(blockIdx.x) % kXcds) * per_xcd + pos;
+  if (pos >= per_xcd || tile >= total) return;
+  const int rt = tile / col_tiles;
+  const int ct = tile % col_tiles;
   int lo = 0, hi = E;  // expert of row tile rt: last e with prefix[e] <= rt
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
@@ -294,7 +303,7 @@ __global__ void __launch_bounds__(kThreads, 2)
 k_bgemm_kgroup(const uint16_t* __restrict__ A, int64_t lda, int M, const uint16_t* __restrict__ B,
                int64_t ldb, int N, const int32_t* __restrict__ ws, int E,
                const uint16_t* __restrict__ zeros, uint16_t* __restrict__ C0,
-               uint16_t* __restrict__ C1, int split, int64_t ldc) {
+               uint16_t* __restrict__ C1, int split, int64_t ldc, int bm, int bn) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStageBytes];
   lds_u8_t* lds = (lds_u8_t*)smem;
   const int32_t* offs = ws + (E + 1);
@@ -303,7 +312,21 @@ k_bgemm_kgroup(const uint16_t* __restrict__ A, int64_t lda, int M, const uint16_
   const int per_e = mt_n * nt_n;
   const int e = order[static_cast<int>(blockIdx.x) / per_e];
   const int t = static_cast<int>(blockIdx.x) % per_e;
-  const int m0 = (t / nt_n) * TM, n0 = (t % nt_n) * TN;
+  // Which output tile of expert e: with bm > 0 (per_e a multiple of 8), the
+  // workgroups of XCD t % 8 take one bm x bn block of the (m, n) tile grid,
+  // chosen on the host so that the A column blocks and B column blocks each
+  // XCD reads (from its own L2) add up to the fewest bytes; else row-major.
+  int mt, nt;
+  if (bm > 0) {
+    const int x = t % kXcds, i = t / kXcds;
+    const int gn = nt_n / bn;  // XCD blocks along n
+    mt = (x / gn) * bm + i / bn;
+    nt = (x % gn) * bn + i % bn;
+  } else {
+    mt = t / nt_n;
+    nt = t % nt_n;
+  }
+  const int m0 = mt * TM, n0 = nt * TN;
   const int r_lo = offs[e], r_hi = offs[e + 1];
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int wm = wave & 1, wn = wave >> 1;
@@ -402,7 +425,7 @@ hipError_t launch_bgemm_rows(const uint16_t* A, int K, const uint16_t* B0, const
                              const int32_t* ws, int E, uint16_t* C, hipStream_t st) {
   if (N_cap == 0) return hipGetLastError();
   const int64_t row_tiles = ceil_div(N_cap, TM) + E;  // at least the real row tiles
-  const int64_t grid = row_tiles * ceil_div(Ncols, TN);
+  const int64_t grid = ceil_div(row_tiles * ceil_div(Ncols, TN), kXcds) * kXcds;
   hipLaunchKernelGGL(k_bgemm_rows, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, st, A, K,
                      B0, B1, ksplit, ldb, strideB, Ncols, ws, E, C);
   return hipGetLastError();
@@ -412,9 +435,25 @@ hipError_t launch_bgemm_kgroup(const uint16_t* A, int64_t lda, int M, const uint
                                int64_t ldb, int N, const int32_t* ws, int E,
                                const uint16_t* zeros, uint16_t* C0, uint16_t* C1, int split,
                                int64_t ldc, hipStream_t st) {
-  const int64_t grid = int64_t(E) * ceil_div(M, TM) * ceil_div(N, TN);
+  const int mt_n = static_cast<int>(ceil_div(M, TM)), nt_n = static_cast<int>(ceil_div(N, TN));
+  const int64_t grid = int64_t(E) * mt_n * nt_n;
+  // the per-XCD tile block (bm x bn, bm | mt_n, bn | nt_n, bm bn = tiles / 8)
+  // that minimizes the column blocks read per XCD: A's M columns are read by
+  // nt_n / bn XCDs, B's N columns by mt_n / bm
+  int bm = 0, bn = 0;
+  if ((mt_n * nt_n) % kXcds == 0) {
+    const int per = mt_n * nt_n / kXcds;
+    int64_t best = -1;
+    for (int a = 1; a <= mt_n; ++a) {
+      if (mt_n % a != 0 || per % a != 0) continue;
+      const int b = per / a;
+      if (nt_n % b != 0) continue;
+      const int64_t cost = int64_t(M) * (nt_n / b) + int64_t(N) * (mt_n / a);
+      if (best < 0 || cost < best) { best = cost; bm = a; bn = b; }
+    }
+  }
   hipLaunchKernelGGL(k_bgemm_kgroup, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, st, A,
-                     lda, M, B, ldb, N, ws, E, zeros, C0, C1, split, ldc);
+                     lda, M, B, ldb, N, ws, E, zeros, C0, C1, split, ldc, bm, bn);
   return hipGetLastError();
 }
 

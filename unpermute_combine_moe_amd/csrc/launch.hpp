@@ -92,6 +92,8 @@ hipError_t launch_dered_combine(const uint16_t* src, const float* coeff, const i
                                 int64_t n, int H, int64_t G, uint16_t* wb, void* ws,
                                 hipStream_t st);
 
+// CUs of the current device rounded down to a multiple of 8 (one per XCD slot)
+int persistent_grid();
 size_t bgemm_sched_bytes(int E);
 hipError_t launch_bgemm_sched(const int32_t* offsets, int E, int64_t N_cap, int32_t* ws,
                               hipStream_t st);

@@ -231,10 +231,12 @@ def step_calls(d):
     return permute, gemm, combine, grad
 
 
-def gemm_grad_op(args, d, n_rows):
-    """The grouped GEMM backward on the layer's own tensors: dy is the unpermute
-    backward's d_permuted, h the forward's. FLOPs counted: 12 N H I (dh, dx and
-    the three weight gradients; the gate/up recompute, 4 N H I more, is not)."""
+def gemm_grad_ops(args, d, n_rows):
+    """The grouped GEMM backward on the layer's own tensors (dy is the unpermute
+    backward's d_permuted, h the forward's), twice: recomputing the gate/up
+    pre-activations, and taking them from a forward that kept them (that
+    forward is timed too). FLOPs counted: 12 N H I (dh, dx and the three weight
+    gradients; the recompute, 4 N H I more, is not)."""
     import torch
     import unpermute_combine_moe_amd as moe
 
@@ -248,11 +250,22 @@ def gemm_grad_op(args, d, n_rows):
     dwu = torch.empty((E, H, I), dtype=bf, device=dev)
     dwd = torch.empty((E, I, H), dtype=bf, device=dev)
     ws = moe.workspace(moe.moe_grouped_gemm_swiglu_grad_workspace_size(E, S, H, I), dev)
-    f = lambda: moe.moe_grouped_gemm_swiglu_grad(d["permuted"], d["offsets"], E, S, H, I, d["wg"],
-                                                 d["wu"], d["wd"], d["h"], d["d_perm"], dx, dwg,
-                                                 dwu, dwd, ws)
-    us, usmin = time_op(f, args.op_iters, None)
-    return op_entry("grouped_gemm_swiglu_grad", us, usmin, flops=12 * n_rows * H * I)
+    pre = torch.empty((S, 2 * I), dtype=torch.float32, device=dev)
+    ops = []
+    fwd = lambda: moe.moe_grouped_gemm_swiglu(d["permuted"], d["offsets"], E, S, H, I, d["wg"],
+                                              d["wu"], d["wd"], d["h"], d["y"], d["ws_g"],
+                                              preact=pre)
+    us, usmin = time_op(fwd, args.op_iters, None)
+    ops.append(op_entry("grouped_gemm_swiglu_keep_preact", us, usmin,
+                        flops=gemm_flops(n_rows, H, I)))
+    for name, p in (("grouped_gemm_swiglu_grad", None),
+                    ("grouped_gemm_swiglu_grad_saved_preact", pre)):
+        f = lambda: moe.moe_grouped_gemm_swiglu_grad(d["permuted"], d["offsets"], E, S, H, I,
+                                                     d["wg"], d["wu"], d["wd"], d["h"],
+                                                     d["d_perm"], dx, dwg, dwu, dwd, ws, preact=p)
+        us, usmin = time_op(f, args.op_iters, None)
+        ops.append(op_entry(name, us, usmin, flops=12 * n_rows * H * I))
+    return ops
 
 
 def run_layer(args, dev):
@@ -580,7 +593,7 @@ def main():
                                         flops=gemm_flops(n_rows, H, I))))
     ops = layer_ops
     if not args.no_ops:
-        ops.append(dict(workload=c["name"], **gemm_grad_op(args, d, n_rows)))
+        ops += [dict(workload=c["name"], **o) for o in gemm_grad_ops(args, d, n_rows)]
         ops = ops + run_ops(args, dev, flush)
         del flush
     cpu = None

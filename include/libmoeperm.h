@@ -201,6 +201,11 @@ moe_status_t moe_rank_to_expert_reorder(const void* x_rank_major, const int32_t*
  *  w_down          bf16 [E, I, H]    in
  *  h               bf16 [N_cap, I]   out
  *  y               bf16 [N_cap, H]   out
+ *  preact          fp32 [N_cap, 2I]  out (nullable, 16-byte aligned): when not
+ *                  NULL, the pre-activations are kept for the backward, g in
+ *                  columns [0, I) and u in [I, 2I) of each written row, exactly
+ *                  the fp32 values the SwiGLU used (rows past
+ *                  expert_offsets[E] are not written)
  * Errors: INVALID_ARG for E outside [1,1024], N_cap < 0 or > INT32_MAX,
  * H <= 0, I <= 0, NULL / misaligned pointers; UNSUPPORTED unless H % 64 == 0
  * and I % 64 == 0, and for H or I above 2^20; WORKSPACE if too small. Offsets that break the stated
@@ -211,14 +216,15 @@ moe_status_t moe_grouped_gemm_swiglu_workspace_size(int32_t E, int64_t N_cap, in
 moe_status_t moe_grouped_gemm_swiglu(const void* x, const int32_t* expert_offsets, int32_t E,
                                      int64_t N_cap, int32_t H, int32_t I, const void* w_gate,
                                      const void* w_up, const void* w_down, void* h, void* y,
-                                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+                                     float* preact, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * moe_grouped_gemm_swiglu_grad -- backward of moe_grouped_gemm_swiglu.
  *
  * [GMM] (the grouped matmul + swiglu of the forward, differentiated for
  * training). For each expert e and row n of its group, with dy = dL/dy:
- *     dh = dy . w_down[e]^T            g, u recomputed from x (fp32, not stored)
+ *     dh = dy . w_down[e]^T            g, u: the forward's preact, or recomputed from x
  *     s = 1 / (1 + exp(-g)),  dg = dh * u * s * (1 + g * (1 - s)),  du = dh * g * s
  *     dx[n] = dg . w_gate[e]^T + du . w_up[e]^T
  *     dw_gate[e] = sum_n x[n]^T dg,  dw_up[e] = sum_n x[n]^T du,
@@ -234,6 +240,12 @@ moe_status_t moe_grouped_gemm_swiglu(const void* x, const int32_t* expert_offset
  *  dx       bf16 [N_cap, H]   out
  *  dw_gate, dw_up  bf16 [E, H, I]   out
  *  dw_down         bf16 [E, I, H]   out
+ *  preact   fp32 [N_cap, 2I]  in (nullable, 16-byte aligned): the forward's
+ *           pre-activations (moe_grouped_gemm_swiglu's preact, same x, weights
+ *           and offsets). When given, the gate/up GEMM is not run again and dh
+ *           is not stored: [dg | du] comes straight out of the dh GEMM. The
+ *           results are the same bits either way; NULL recomputes g and u
+ *           (2 N_cap H I more multiply-adds, no [N_cap, 2I] fp32 buffer).
  *  workspace  moe_grouped_gemm_swiglu_grad_workspace_size bytes, 256-byte
  *             aligned (about 6 * N_cap * I bytes: dh and [dg | du])
  * Errors: as moe_grouped_gemm_swiglu (INVALID_ARG, UNSUPPORTED unless
@@ -245,8 +257,8 @@ moe_status_t moe_grouped_gemm_swiglu_grad(const void* x, const int32_t* expert_o
                                           int64_t N_cap, int32_t H, int32_t I, const void* w_gate,
                                           const void* w_up, const void* w_down, const void* h,
                                           const void* dy, void* dx, void* dw_gate, void* dw_up,
-                                          void* dw_down, void* workspace, size_t workspace_bytes,
-                                          hipStream_t stream);
+                                          void* dw_down, const float* preact, void* workspace,
+                                          size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * moe_unpermute_combine -- weighted top-K combine back to token order.

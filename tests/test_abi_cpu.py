@@ -58,7 +58,7 @@ def test_status_strings_and_version(lib):
     assert binding.status_str(0) == "MOE_OK"
     assert binding.status_str(3) == "MOE_ERR_WORKSPACE"
     assert binding.status_str(99) == "MOE_ERR_UNKNOWN"
-    assert lib.moe_abi_version() == 2
+    assert lib.moe_abi_version() == 3
 
 
 def test_workspace_sizes(lib):
@@ -182,9 +182,9 @@ def test_reorder_checks(lib):
     assert _reorder(lib, wsb=8) == WORKSPACE
 
 
-def _gemm(lib, x=P, off=P, E=8, N=1000, H=256, I=128, wg=P, wu=P, wd=P, h=P, y=P, ws=P,
-          wsb=1 << 20):
-    return lib.moe_grouped_gemm_swiglu(x, off, E, N, H, I, wg, wu, wd, h, y, ws, wsb, None)
+def _gemm(lib, x=P, off=P, E=8, N=1000, H=256, I=128, wg=P, wu=P, wd=P, h=P, y=P, pre=None,
+          ws=P, wsb=1 << 20):
+    return lib.moe_grouped_gemm_swiglu(x, off, E, N, H, I, wg, wu, wd, h, y, pre, ws, wsb, None)
 
 
 @no_gpu
@@ -200,8 +200,29 @@ def test_gemm_checks(lib):
     assert _gemm(lib, off=None) == INVALID
     assert _gemm(lib, wd=P + 4) == INVALID
     assert _gemm(lib, y=None) == INVALID
+    assert _gemm(lib, pre=P + 8) == INVALID             # preact must be 16-byte aligned
     assert _gemm(lib, ws=None) == WORKSPACE
     assert _gemm(lib, wsb=4) == WORKSPACE
+
+
+def _ggrad(lib, x=P, off=P, E=8, N=1000, H=256, I=128, wg=P, wu=P, wd=P, h=P, dy=P, dx=P,
+           dwg=P, dwu=P, dwd=P, pre=None, ws=P, wsb=1 << 30):
+    return lib.moe_grouped_gemm_swiglu_grad(x, off, E, N, H, I, wg, wu, wd, h, dy, dx, dwg, dwu,
+                                            dwd, pre, ws, wsb, None)
+
+
+@no_gpu
+def test_gemm_grad_checks(lib):
+    assert _ggrad(lib, E=0) == INVALID
+    assert _ggrad(lib, N=-1) == INVALID
+    assert _ggrad(lib, H=96) == UNSUPPORTED
+    assert _ggrad(lib, I=(1 << 20) + 64) == UNSUPPORTED
+    assert _ggrad(lib, dx=None) == INVALID
+    assert _ggrad(lib, dwd=P + 4) == INVALID
+    assert _ggrad(lib, pre=P + 8) == INVALID             # preact must be 16-byte aligned
+    assert _ggrad(lib, ws=None) == WORKSPACE
+    assert _ggrad(lib, ws=P + 16) == WORKSPACE           # 256-byte aligned
+    assert _ggrad(lib, wsb=4) == WORKSPACE
 
 
 def _combine(lib, eo=P, N=100, ros=P, rmap=None, ids=P, probs=P, T=50, K=2, H=64, E=8, sp=None,

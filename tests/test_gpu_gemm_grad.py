@@ -115,3 +115,42 @@ def test_gemm_grad_config1(moe_lib):
                                      g["w_down"], dy)
     _check(got, ref, p["permuted"], p["expert_offsets"], g["w_gate"], g["w_up"], g["w_down"], dy)
 
+
+
+@pytest.mark.parametrize("counts,H,I,seed", [
+    ([5, 0, 130, 1, 0, 64], 128, 64, 21),
+    ([300, 2, 0, 129], 320, 192, 22),
+    ([0, 0, 0], 64, 128, 23),
+])
+def test_gemm_saved_preact(moe_lib, counts, H, I, seed):
+    """The forward's optional pre-activations: g and u in fp32 as the SwiGLU
+    used them (against fp64 x.W within the fp32 accumulation bound), h and y
+    unchanged by keeping them, and a backward from them that gives the same
+    bits as the one that recomputes them."""
+    x, off, wg, wu, wd, dy = _data(seed, counts, H, I)
+    E = len(counts)
+    n = int(off[-1])
+    print(f"saved pre-activations N={x.shape[0]} E={E} H={H} I={I} rows={n}", flush=True)
+    xd, od = to_dev_bf16(x), to_dev(off)
+    wgd, wud, wdd = to_dev_bf16(wg), to_dev_bf16(wu), to_dev_bf16(wd)
+    h0, y0 = moe_lib.grouped_gemm_alloc(xd, od, wgd, wud, wdd)
+    h1, y1, pre = moe_lib.grouped_gemm_alloc(xd, od, wgd, wud, wdd, keep_preact=True)
+    dyd = to_dev_bf16(dy)
+    g0 = moe_lib.grouped_gemm_grad_alloc(xd, od, wgd, wud, wdd, h0, dyd)
+    g1 = moe_lib.grouped_gemm_grad_alloc(xd, od, wgd, wud, wdd, h0, dyd, preact=pre)
+    torch.cuda.synchronize()
+    assert torch.equal(h0[:n], h1[:n]) and torch.equal(y0[:n], y1[:n])
+    for k in g0:
+        a, b = (g0[k][:n], g1[k][:n]) if k == "dx" else (g0[k], g1[k])
+        assert torch.equal(a, b), k
+    P = pre.cpu().numpy().astype(np.float64)
+    for e in range(E):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if lo == hi:
+            continue
+        X = f64(x[lo:hi])
+        for j, w in ((0, wg[e]), (1, wu[e])):
+            ref = X @ f64(w)
+            bound = 2.0 ** -13 * (np.abs(X) @ np.abs(f64(w))) + 1e-30
+            err = np.abs(P[lo:hi, j * I:(j + 1) * I] - ref)
+            assert np.all(err <= bound), f"expert {e} {'gu'[j]}: worst err/bound {np.max(err / bound):.3f}"

@@ -127,7 +127,8 @@ def test_layer_unpermute_grad_h2048(layer, ref):
 
 def test_layer_gemm_grad_complete(layer, ref):
     """The grouped GEMM backward at the layer's shapes: every dx row and the
-    weight gradients of every expert (the empty ones must be zero)."""
+    weight gradients of every expert (the empty ones must be zero), and the
+    same bits from the path that takes the forward's saved pre-activations."""
     d = layer["d"]
     g = d["host"]
     c = d["cfg"]
@@ -136,10 +137,17 @@ def test_layer_gemm_grad_complete(layer, ref):
     off = p["expert_offsets"]
     x = p["permuted"]
     dy = W.normal_bf16(np.random.default_rng(12), x.shape)
-    xd, od = to_dev_bf16(x), to_dev(off)
-    h, _ = moe.grouped_gemm_alloc(xd, od, d["wg"], d["wu"], d["wd"])
-    got_t = moe.grouped_gemm_grad_alloc(xd, od, d["wg"], d["wu"], d["wd"], h, to_dev_bf16(dy))
+    xd, od, dyd = to_dev_bf16(x), to_dev(off), to_dev_bf16(dy)
+    h, _, pre = moe.grouped_gemm_alloc(xd, od, d["wg"], d["wu"], d["wd"], keep_preact=True)
+    got_t = moe.grouped_gemm_grad_alloc(xd, od, d["wg"], d["wu"], d["wd"], h, dyd)
+    # the path that takes the forward's pre-activations gives the same bits
+    saved = moe.grouped_gemm_grad_alloc(xd, od, d["wg"], d["wu"], d["wd"], h, dyd, preact=pre)
     torch.cuda.synchronize()
+    n = int(off[-1])
+    for k in got_t:
+        a, b = (got_t[k][:n], saved[k][:n]) if k == "dx" else (got_t[k], saved[k])
+        assert torch.equal(a, b), f"{k}: saved pre-activations differ from recomputation"
+    del saved, pre
     got = {k: f64(bits(v)) for k, v in got_t.items()}
     del got_t, h
     print("oracle: fp64 FFN backward of all routed rows", flush=True)

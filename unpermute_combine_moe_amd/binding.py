@@ -81,7 +81,7 @@ def load(path: str = LIB_PATH):
                                                _vp, _vp, _vp, ctypes.c_size_t, _vp]
     lib.moe_grouped_gemm_swiglu_workspace_size.argtypes = [_i32, _i64, _i32, _i32, sz]
     lib.moe_grouped_gemm_swiglu.argtypes = [_vp, _vp, _i32, _i64, _i32, _i32, _vp, _vp, _vp, _vp,
-                                            _vp, _vp, ctypes.c_size_t, _vp]
+                                            _vp, _vp, _vp, ctypes.c_size_t, _vp]
     lib.moe_unpermute_combine.argtypes = [_vp, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _i64, _i32,
                                           _i32, _i32, ctypes.POINTER(MoeSpecialExperts), _vp, _vp,
                                           _vp]
@@ -99,7 +99,7 @@ def load(path: str = LIB_PATH):
                                              ctypes.c_size_t, _vp]
     lib.moe_grouped_gemm_swiglu_grad_workspace_size.argtypes = [_i32, _i64, _i32, _i32, sz]
     lib.moe_grouped_gemm_swiglu_grad.argtypes = [_vp, _vp, _i32, _i64, _i32, _i32, _vp, _vp, _vp,
-                                                 _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                 _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                                  ctypes.c_size_t, _vp]
     for name in EXPORTS[2:]:
         getattr(lib, name).restype = ctypes.c_int
@@ -236,12 +236,13 @@ def moe_rank_to_expert_reorder(x_rank_major, counts, R, E_local, N, H, y_expert_
 
 
 def moe_grouped_gemm_swiglu(x, expert_offsets, E, N_cap, H, I, w_gate, w_up, w_down, h, y, ws,
-                            stream=None):
+                            stream=None, preact=None):
     _check(load().moe_grouped_gemm_swiglu(
         _ptr(x, _BF16, "x"), _ptr(expert_offsets, _I32, "expert_offsets"), E, N_cap, H, I,
         _ptr(w_gate, _BF16, "w_gate"), _ptr(w_up, _BF16, "w_up"), _ptr(w_down, _BF16, "w_down"),
-        _ptr(h, _BF16, "h"), _ptr(y, _BF16, "y"), _ptr(ws, None, "workspace"),
-        ws.numel() if ws is not None else 0, _stream(stream)), "moe_grouped_gemm_swiglu")
+        _ptr(h, _BF16, "h"), _ptr(y, _BF16, "y"), _ptr(preact, _F32, "preact"),
+        _ptr(ws, None, "workspace"), ws.numel() if ws is not None else 0, _stream(stream)),
+        "moe_grouped_gemm_swiglu")
 
 
 def make_special(num_zero=0, num_copy=0, num_const=0, ori_x=None, alpha1=None, alpha2=None,
@@ -340,14 +341,15 @@ def moe_grouped_gemm_swiglu_grad_workspace_size(E, N_cap, H, I) -> int:
 
 
 def moe_grouped_gemm_swiglu_grad(x, expert_offsets, E, N_cap, H, I, w_gate, w_up, w_down, h, dy,
-                                 dx, dw_gate, dw_up, dw_down, ws, stream=None):
+                                 dx, dw_gate, dw_up, dw_down, ws, stream=None, preact=None):
     _check(load().moe_grouped_gemm_swiglu_grad(
         _ptr(x, _BF16, "x"), _ptr(expert_offsets, _I32, "expert_offsets"), E, N_cap, H, I,
         _ptr(w_gate, _BF16, "w_gate"), _ptr(w_up, _BF16, "w_up"), _ptr(w_down, _BF16, "w_down"),
         _ptr(h, _BF16, "h"), _ptr(dy, _BF16, "dy"), _ptr(dx, _BF16, "dx"),
         _ptr(dw_gate, _BF16, "dw_gate"), _ptr(dw_up, _BF16, "dw_up"),
-        _ptr(dw_down, _BF16, "dw_down"), _ptr(ws, None, "workspace"),
-        ws.numel() if ws is not None else 0, _stream(stream)), "moe_grouped_gemm_swiglu_grad")
+        _ptr(dw_down, _BF16, "dw_down"), _ptr(preact, _F32, "preact"),
+        _ptr(ws, None, "workspace"), ws.numel() if ws is not None else 0, _stream(stream)),
+        "moe_grouped_gemm_swiglu_grad")
 
 
 # --------------------------------------------------------------------------- allocating helpers
@@ -390,16 +392,19 @@ def reorder_alloc(x_rank_major, counts, R, E_local, N=None, *, rows: bool = True
     return out
 
 
-def grouped_gemm_alloc(x, expert_offsets, w_gate, w_up, w_down, *, stream=None):
+def grouped_gemm_alloc(x, expert_offsets, w_gate, w_up, w_down, *, stream=None,
+                       keep_preact=False):
+    """Returns (h, y), or (h, y, preact) with keep_preact (fp32 [N_cap, 2I], g | u)."""
     E, H, I = w_gate.shape
     N_cap = x.shape[0]
     dev = x.device
     h = torch.empty((N_cap, I), dtype=_BF16, device=dev)
     y = torch.empty((N_cap, H), dtype=_BF16, device=dev)
+    preact = torch.empty((N_cap, 2 * I), dtype=_F32, device=dev) if keep_preact else None
     ws = workspace(moe_grouped_gemm_swiglu_workspace_size(E, N_cap, H, I), dev)
     moe_grouped_gemm_swiglu(x, expert_offsets, E, N_cap, H, I, w_gate, w_up, w_down, h, y, ws,
-                            stream)
-    return h, y
+                            stream, preact=preact)
+    return (h, y, preact) if keep_preact else (h, y)
 
 
 def combine_alloc(expert_out, row_of_slot, expert_ids, probs, num_experts, *, row_map=None,
@@ -491,8 +496,11 @@ def dered_combine_alloc(outer_output, router_coeff, dispatch_indices, G, *, stre
     return wb
 
 
-def grouped_gemm_grad_alloc(x, expert_offsets, w_gate, w_up, w_down, h, dy, *, stream=None):
-    """Backward of the grouped SwiGLU FFN. Returns dict(dx, dw_gate, dw_up, dw_down)."""
+def grouped_gemm_grad_alloc(x, expert_offsets, w_gate, w_up, w_down, h, dy, *, stream=None,
+                            preact=None):
+    """Backward of the grouped SwiGLU FFN. Returns dict(dx, dw_gate, dw_up, dw_down).
+    preact: the forward's pre-activations (grouped_gemm_alloc(keep_preact=True)), or None
+    to recompute them."""
     E, H, I = w_gate.shape
     N_cap = x.shape[0]
     dev = x.device
@@ -503,5 +511,5 @@ def grouped_gemm_grad_alloc(x, expert_offsets, w_gate, w_up, w_down, h, dy, *, s
     ws = workspace(moe_grouped_gemm_swiglu_grad_workspace_size(E, N_cap, H, I), dev)
     moe_grouped_gemm_swiglu_grad(x, expert_offsets, E, N_cap, H, I, w_gate, w_up, w_down, h, dy,
                                  out["dx"], out["dw_gate"], out["dw_up"], out["dw_down"], ws,
-                                 stream)
+                                 stream, preact=preact)
     return out

@@ -13,7 +13,7 @@
 
 namespace {
 
-constexpr int32_t kAbiVersion = 2;
+constexpr int32_t kAbiVersion = 3;
 
 inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 // a row tensor: non-null and 16-byte aligned
@@ -204,18 +204,20 @@ MOE_API moe_status_t moe_grouped_gemm_swiglu(const void* x, const int32_t* exper
                                              int32_t E, int64_t N_cap, int32_t H, int32_t I,
                                              const void* w_gate, const void* w_up,
                                              const void* w_down, void* h, void* y,
-                                             void* workspace, size_t workspace_bytes,
-                                             hipStream_t stream) {
+                                             float* preact, void* workspace,
+                                             size_t workspace_bytes, hipStream_t stream) {
   if (moe_status_t s = check_gemm_sizes(E, N_cap, H, I)) return s;
   if (!word_ok(expert_offsets)) return MOE_ERR_INVALID_ARG;
   if (!row_ok(w_gate) || !row_ok(w_up) || !row_ok(w_down)) return MOE_ERR_INVALID_ARG;
   if (N_cap > 0 && (!row_ok(x) || !row_ok(h) || !row_ok(y))) return MOE_ERR_INVALID_ARG;
+  if (preact != nullptr && !aligned(preact, 16)) return MOE_ERR_INVALID_ARG;
   const size_t need = moe::gemm_workspace_bytes(E, N_cap, H, I);
   if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 4))
     return MOE_ERR_WORKSPACE;
   return hip_status(moe::launch_grouped_gemm_swiglu(u16(x), expert_offsets, E, N_cap, H, I,
                                                     u16(w_gate), u16(w_up), u16(w_down), u16(h),
-                                                    u16(y), workspace, stream));
+                                                    u16(y), N_cap > 0 ? preact : nullptr,
+                                                    workspace, stream));
 }
 
 MOE_API moe_status_t moe_grouped_gemm_swiglu_grad_workspace_size(int32_t E, int64_t N_cap,
@@ -233,8 +235,8 @@ MOE_API moe_status_t moe_grouped_gemm_swiglu_grad_workspace_size(int32_t E, int6
 MOE_API moe_status_t moe_grouped_gemm_swiglu_grad(
     const void* x, const int32_t* expert_offsets, int32_t E, int64_t N_cap, int32_t H, int32_t I,
     const void* w_gate, const void* w_up, const void* w_down, const void* h, const void* dy,
-    void* dx, void* dw_gate, void* dw_up, void* dw_down, void* workspace, size_t workspace_bytes,
-    hipStream_t stream) {
+    void* dx, void* dw_gate, void* dw_up, void* dw_down, const float* preact, void* workspace,
+    size_t workspace_bytes, hipStream_t stream) {
   if (E < 1 || E > MOE_MAX_EXPERTS || N_cap < 0 || N_cap > INT32_MAX || H <= 0 || I <= 0)
     return MOE_ERR_INVALID_ARG;
   if (H % 64 != 0 || I % 64 != 0) return MOE_ERR_UNSUPPORTED;
@@ -244,12 +246,14 @@ MOE_API moe_status_t moe_grouped_gemm_swiglu_grad(
     return MOE_ERR_INVALID_ARG;
   if (N_cap > 0 && (!row_ok(x) || !row_ok(h) || !row_ok(dy) || !row_ok(dx)))
     return MOE_ERR_INVALID_ARG;
+  if (preact != nullptr && !aligned(preact, 16)) return MOE_ERR_INVALID_ARG;
   if (workspace == nullptr || !aligned(workspace, 256) ||
       workspace_bytes < moe::gemm_grad_workspace_bytes(E, N_cap, H, I))
     return MOE_ERR_WORKSPACE;
   return hip_status(moe::launch_grouped_gemm_swiglu_grad(
       u16(x), expert_offsets, E, N_cap, H, I, u16(w_gate), u16(w_up), u16(w_down), u16(h), u16(dy),
-      u16(dx), u16(dw_gate), u16(dw_up), u16(dw_down), workspace, stream));
+      u16(dx), u16(dw_gate), u16(dw_up), u16(dw_down), N_cap > 0 ? preact : nullptr, workspace,
+      stream));
 }
 
 // --------------------------------------------------------------------------- combine

@@ -119,6 +119,15 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 __host__ __device__ constexpr int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// SwiGLU derivative for one element: with s = 1 / (1 + exp(-g)),
+// dg = d u s (1 + g (1 - s)) and du = d g s. Every kernel that forms [dg | du]
+// calls this one function, so the same g, u and d give the same bits.
+__device__ __forceinline__ void swiglu_grad(float d, float g, float u, float* dg, float* du) {
+  const float s = __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+  *dg = d * u * s * (1.0f + g * (1.0f - s));
+  *du = d * g * s;
+}
+
 // ---- staged-operand ring of the GEMM kernels
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:

@@ -159,6 +159,7 @@ __device__ __forceinline__ bf16x8_t lds_read_a(const lds_u8_t* base, int slot) {
 }
 
 // kMode 0: gate/up + SwiGLU -> h.  kMode 1: down -> y.
+// kMode 0 with preact != nullptr also stores g and u (fp32) as preact [N, 2 Ncols].
 // kMode 2: gate/up recomputed for the backward; with dh = aux [N, Ncols], the
 // epilogue writes C [N, 2 * Ncols] = [dg | du], dg = dh * u * s (1 + g (1 - s)),
 // du = dh * g * s, s = 1 / (1 + exp(-g)) (the SwiGLU derivative).
@@ -166,7 +167,7 @@ template <int kMode>
 __global__ void __launch_bounds__(Layout<kMode>::kThreads, 1)
 k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0,
        const uint16_t* __restrict__ B1, int Ncols, const int32_t* __restrict__ ws, int E,
-       uint16_t* __restrict__ C, const uint16_t* __restrict__ aux) {
+       uint16_t* __restrict__ C, const uint16_t* __restrict__ aux, float* __restrict__ preact) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes];
   // row-tile prefix and clamped expert offsets, staged once per workgroup so the
   // per-tile expert lookup is a binary search in LDS
@@ -494,14 +495,25 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
                 const float u = acc[i][jj + EP::kOutFrags][4 * q + k];
                 v[k] = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
               } else if (kMode == 2) {
-                const float g = acc[i][jj][4 * q + k];
-                const float u = acc[i][jj + EP::kOutFrags][4 * q + k];
-                const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g));
-                v[k] = d[k] * u * sg * (1.0f + g * (1.0f - sg));  // dg
-                w[k] = d[k] * g * sg;                              // du
+                swiglu_grad(d[k], acc[i][jj][4 * q + k], acc[i][jj + EP::kOutFrags][4 * q + k],
+                            &v[k], &w[k]);
               } else {
                 v[k] = acc[i][jj][4 * q + k];
               }
+            }
+            if (kMode == 0 && preact != nullptr && row < ci.row_end && col < Ncols) {
+              // the pre-activations for the backward: g at column col, u at
+              // Ncols + col of the fp32 [N, 2 Ncols] buffer (not counted in the
+              // vmcnt waits, which only makes those waits stricter)
+              float* dst = preact + int64_t(row) * (2 * Ncols) + col;
+              const u32x4_t gv = {__float_as_uint(acc[i][jj][4 * q]), __float_as_uint(acc[i][jj][4 * q + 1]),
+                                  __float_as_uint(acc[i][jj][4 * q + 2]), __float_as_uint(acc[i][jj][4 * q + 3])};
+              const u32x4_t uv = {__float_as_uint(acc[i][jj + EP::kOutFrags][4 * q]),
+                                  __float_as_uint(acc[i][jj + EP::kOutFrags][4 * q + 1]),
+                                  __float_as_uint(acc[i][jj + EP::kOutFrags][4 * q + 2]),
+                                  __float_as_uint(acc[i][jj + EP::kOutFrags][4 * q + 3])};
+              __builtin_nontemporal_store(gv, reinterpret_cast<u32x4_t*>(dst));
+              __builtin_nontemporal_store(uv, reinterpret_cast<u32x4_t*>(dst + Ncols));
             }
             // chunk of these four columns in the staged row, and which half of it
             const int chunk = 4 * jj + q;
@@ -571,22 +583,25 @@ size_t gemm_workspace_bytes(int E, int64_t /*N_cap*/, int /*H*/, int /*I*/) {
 hipError_t launch_grouped_gemm_swiglu(const uint16_t* x, const int32_t* offsets, int E,
                                       int64_t N_cap, int H, int I, const uint16_t* wg,
                                       const uint16_t* wu, const uint16_t* wd, uint16_t* h,
-                                      uint16_t* y, void* ws, hipStream_t st) {
+                                      uint16_t* y, float* preact, void* ws, hipStream_t st) {
   int32_t* w = static_cast<int32_t*>(ws);
   hipLaunchKernelGGL(k_gemm_sched, dim3(1), dim3(kSchedThreads), 0, st, offsets, E, N_cap, w);
   if (N_cap == 0) return hipGetLastError();
   const int G = persistent_grid();
   hipLaunchKernelGGL(k_gemm<0>, dim3(G), dim3(Layout<0>::kThreads), 0, st, x, H, wg, wu, I, w, E,
-                     h, nullptr);
+                     h, nullptr, preact);
   hipLaunchKernelGGL(k_gemm<1>, dim3(G), dim3(Layout<1>::kThreads), 0, st, h, I, wd, nullptr, H, w,
-                     E, y,
-                     nullptr);
+                     E, y, nullptr, nullptr);
   return hipGetLastError();
 }
 
 // Backward: dh = dy Wd^T (row-grouped), [dg | du] from the recomputed gate/up
 // tiles (mode 2), dx = [dg | du] [Wg ; Wu]^T (row-grouped), dWd = h^T dy and
-// [dWg | dWu] = x^T [dg | du] (sums over each expert's rows).
+// [dWg | dWu] = x^T [dg | du] (sums over each expert's rows). With the
+// forward's fp32 pre-activations (preact) the gate/up GEMM is not run again:
+// the dh GEMM's epilogue forms [dg | du] from them directly, with the same
+// values and the same arithmetic as the recomputing path, so both paths give
+// the same bits.
 // ws layout: forward tables | backward tables | zeros[256 B]
 //            | dh [N_cap, I] bf16 | dgu [N_cap, 2I] bf16
 size_t gemm_grad_layout(int E, int64_t N_cap, int I, size_t* off_bt, size_t* off_zero,
@@ -614,8 +629,8 @@ hipError_t launch_grouped_gemm_swiglu_grad(const uint16_t* x, const int32_t* off
                                            int64_t N_cap, int H, int I, const uint16_t* wg,
                                            const uint16_t* wu, const uint16_t* wd,
                                            const uint16_t* h, const uint16_t* dy, uint16_t* dx,
-                                           uint16_t* dwg, uint16_t* dwu, uint16_t* dwd, void* ws,
-                                           hipStream_t st) {
+                                           uint16_t* dwg, uint16_t* dwu, uint16_t* dwd,
+                                           const float* preact, void* ws, hipStream_t st) {
   size_t off_bt, off_zero, off_dh, off_dgu;
   gemm_grad_layout(E, N_cap, I, &off_bt, &off_zero, &off_dh, &off_dgu);
   char* base = static_cast<char*>(ws);
@@ -625,19 +640,29 @@ hipError_t launch_grouped_gemm_swiglu_grad(const uint16_t* x, const int32_t* off
   uint16_t* dh = reinterpret_cast<uint16_t*>(base + off_dh);
   uint16_t* dgu = reinterpret_cast<uint16_t*>(base + off_dgu);
   hipLaunchKernelGGL(k_fill_zero, dim3(1), dim3(64), 0, st, reinterpret_cast<uint32_t*>(zeros), 64);
-  hipLaunchKernelGGL(k_gemm_sched, dim3(1), dim3(kSchedThreads), 0, st, offsets, E, N_cap, w);
+  if (preact == nullptr)
+    hipLaunchKernelGGL(k_gemm_sched, dim3(1), dim3(kSchedThreads), 0, st, offsets, E, N_cap, w);
   hipError_t err = launch_bgemm_sched(offsets, E, N_cap, bt, st);
   if (err != hipSuccess) return err;
   if (N_cap > 0) {
-    // dh = dy Wd^T: B_e = Wd[e] as [I][H]
-    err = launch_bgemm_rows(dy, H, wd, wd, H, H, int64_t(I) * H, I, N_cap, bt, E, dh, st);
-    if (err != hipSuccess) return err;
-    // [dg | du] from the recomputed gate and up tiles
-    const int G = persistent_grid();
-    hipLaunchKernelGGL(k_gemm<2>, dim3(G), dim3(Layout<2>::kThreads), 0, st, x, H, wg, wu, I, w, E,
-                       dgu, dh);
+    if (preact != nullptr) {
+      // [dg | du] straight from the dh GEMM (dy Wd^T, B_e = Wd[e] as [I][H])
+      err = launch_bgemm_rows(dy, H, wd, wd, H, H, int64_t(I) * H, I, N_cap, bt, E, dgu, preact,
+                              st);
+      if (err != hipSuccess) return err;
+    } else {
+      // dh = dy Wd^T: B_e = Wd[e] as [I][H]
+      err = launch_bgemm_rows(dy, H, wd, wd, H, H, int64_t(I) * H, I, N_cap, bt, E, dh, nullptr,
+                              st);
+      if (err != hipSuccess) return err;
+      // [dg | du] from the recomputed gate and up tiles
+      const int G = persistent_grid();
+      hipLaunchKernelGGL(k_gemm<2>, dim3(G), dim3(Layout<2>::kThreads), 0, st, x, H, wg, wu, I, w,
+                         E, dgu, dh, nullptr);
+    }
     // dx = [dg | du] [Wg ; Wu]^T: B_e = Wg[e], Wu[e] as [H][I] side by side along k
-    err = launch_bgemm_rows(dgu, 2 * I, wg, wu, I, I, int64_t(H) * I, H, N_cap, bt, E, dx, st);
+    err = launch_bgemm_rows(dgu, 2 * I, wg, wu, I, I, int64_t(H) * I, H, N_cap, bt, E, dx, nullptr,
+                            st);
     if (err != hipSuccess) return err;
   }
   // dWd = h^T dy  ([E, I, H]),  [dWg | dWu] = x^T [dg | du]  ([E, H, I] each)

@@ -89,18 +89,15 @@ __device__ __forceinline__ void st_lds16(lds_u8_t* t, int slot, const uint4& v) 
   *(__attribute__((address_space(3))) u32x4_t*)(t + slot * 16) = u;
 }
 
-// Stores of one wave's 64 x 64 accumulator block, rows m0 .. m0 + 63 and
-// columns n0 .. n0 + 63 (columns at or past `split` go to C1 at column
-// n - split; rows >= m_end and columns >= n_end are not stored). In registers
-// a lane holds row m0 + 32 i + lane % 32 and four consecutive columns
-// n0 + 32 j + 8 q + 4 (lane / 32), so a direct store would cover 32 rows x 16 B.
-// The block goes through the wave's 8 KB staging area `stg` in LDS as
-// [64 rows][128 B] (16-byte chunks XOR-swizzled by (row / 2) % 8, which keeps
-// both the column-wise writes and the row-wise reads free of bank conflicts)
-// and is written back 16 B per lane, 8 rows x 128 B per store.
-__device__ __forceinline__ void store_block(const f32x16_t acc[2][2], lds_u8_t* stg, int m0,
-                                            int m_end, int n0, int n_end, int split,
-                                            uint16_t* C0, uint16_t* C1, int64_t ldc, int lane) {
+// Epilogue of one wave's 64 x 64 accumulator block, rows m0 .. m0 + 63 and
+// columns n0 .. n0 + 63. In registers a lane holds row m0 + 32 i + lane % 32
+// and four consecutive columns n0 + 32 j + 8 q + 4 (lane / 32), so a direct
+// store would cover 32 rows x 16 B. The block goes through the wave's 8 KB
+// staging area `stg` in LDS as [64 rows][128 B] of bf16 (16-byte chunks
+// XOR-swizzled by (row / 2) % 8, which keeps both the column-wise writes and
+// the row-wise reads free of bank conflicts) and is read back 16 B (8 columns)
+// per lane, 8 rows x 128 B per wave-wide access.
+__device__ __forceinline__ void stage_block(const f32x16_t acc[2][2], lds_u8_t* stg, int lane) {
   typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -118,15 +115,72 @@ __device__ __forceinline__ void store_block(const f32x16_t acc[2][2], lds_u8_t* 
   }
   // the wave's own writes have completed before it reads them back
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+// Staged row r (0..63), 16-byte chunk c (columns 8 c .. 8 c + 7 of the block).
+__device__ __forceinline__ u32x4_t staged_chunk(const lds_u8_t* stg, int r, int c) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(
+      stg + r * 128 + (c ^ ((r >> 1) & 7)) * 16);
+}
+
+// The block stored as bf16 (columns at or past `split` go to C1 at column
+// n - split; rows >= m_end and columns >= n_end are not stored).
+__device__ __forceinline__ void store_block(const f32x16_t acc[2][2], lds_u8_t* stg, int m0,
+                                            int m_end, int n0, int n_end, int split,
+                                            uint16_t* C0, uint16_t* C1, int64_t ldc, int lane) {
+  stage_block(acc, stg, lane);
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     const int r = 8 * t + lane / 8, c = lane % 8;
-    const u32x4_t v = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(
-        stg + r * 128 + (c ^ ((r >> 1) & 7)) * 16);
+    const u32x4_t v = staged_chunk(stg, r, c);
     const int m = m0 + r, n = n0 + 8 * c;
     if (m < m_end && n < n_end) {
       uint16_t* dst = n < split ? C0 + int64_t(m) * ldc + n : C1 + int64_t(m) * ldc + (n - split);
       *reinterpret_cast<u32x4_t*>(dst) = v;
+    }
+  }
+}
+
+// The block taken as dh (rows m, columns n < I), rounded to bf16 as a stored dh
+// would be, and turned into the SwiGLU gradients with the forward's fp32
+// pre-activations g = preact[m][n], u = preact[m][I + n]: dg goes to
+// dgu[m][n] and du to dgu[m][I + n] (bf16). dh itself is never stored.
+__device__ __forceinline__ void store_block_swiglu_grad(const f32x16_t acc[2][2], lds_u8_t* stg,
+                                                        int m0, int m_end, int n0, int I,
+                                                        const float* __restrict__ preact,
+                                                        uint16_t* __restrict__ dgu, int lane) {
+  stage_block(acc, stg, lane);
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int r = 8 * t + lane / 8, c = lane % 8;
+    const u32x4_t v = staged_chunk(stg, r, c);
+    const int m = m0 + r, n = n0 + 8 * c;
+    if (m < m_end && n < I) {
+      const float* pg = preact + int64_t(m) * (2 * I) + n;
+      const u32x4_t g0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(pg));
+      const u32x4_t g1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(pg + 4));
+      const u32x4_t u0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(pg + I));
+      const u32x4_t u1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(pg + I + 4));
+      const float g[8] = {__uint_as_float(g0.x), __uint_as_float(g0.y), __uint_as_float(g0.z),
+                          __uint_as_float(g0.w), __uint_as_float(g1.x), __uint_as_float(g1.y),
+                          __uint_as_float(g1.z), __uint_as_float(g1.w)};
+      const float u[8] = {__uint_as_float(u0.x), __uint_as_float(u0.y), __uint_as_float(u0.z),
+                          __uint_as_float(u0.w), __uint_as_float(u1.x), __uint_as_float(u1.y),
+                          __uint_as_float(u1.z), __uint_as_float(u1.w)};
+      const uint32_t dw[4] = {v.x, v.y, v.z, v.w};
+      float dg[8], du[8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        swiglu_grad(bf16_lo(dw[k]), g[2 * k], u[2 * k], &dg[2 * k], &du[2 * k]);
+        swiglu_grad(bf16_hi(dw[k]), g[2 * k + 1], u[2 * k + 1], &dg[2 * k + 1], &du[2 * k + 1]);
+      }
+      const u32x4_t og = {pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]),
+                          pack_bf16x2(dg[4], dg[5]), pack_bf16x2(dg[6], dg[7])};
+      const u32x4_t ou = {pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]),
+                          pack_bf16x2(du[4], du[5]), pack_bf16x2(du[6], du[7])};
+      uint16_t* dst = dgu + int64_t(m) * (2 * I) + n;
+      *reinterpret_cast<u32x4_t*>(dst) = og;
+      *reinterpret_cast<u32x4_t*>(dst + I) = ou;
     }
   }
 }
@@ -175,10 +229,14 @@ k_bgemm_sched(const int32_t* __restrict__ offsets, int E, int64_t N_cap, int32_t
 // Row-grouped C = A B^T. A [rows][K] (lda = K), B_e = B0/B1 + e * strideB with
 // element (n, k) at n * ldb + k for k < ksplit (B0) and n * ldb + k - ksplit
 // (B1) otherwise. Grid: an upper bound of the row tiles times the column tiles.
+// kSwigluGrad: C is taken as dh and the epilogue writes [dg | du] instead
+// (store_block_swiglu_grad, with Ncols = I and C = dgu [rows, 2 I]).
+template <bool kSwigluGrad>
 __global__ void __launch_bounds__(kThreads, 2)
 k_bgemm_rows(const uint16_t* __restrict__ A, int K, const uint16_t* __restrict__ B0,
              const uint16_t* __restrict__ B1, int ksplit, int64_t ldb, int64_t strideB, int Ncols,
-             const int32_t* __restrict__ ws, int E, uint16_t* __restrict__ C) {
+             const int32_t* __restrict__ ws, int E, uint16_t* __restrict__ C,
+             const float* __restrict__ preact) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStageBytes];
   lds_u8_t* lds = (lds_u8_t*)smem;
   const int32_t* prefix = ws;
@@ -291,8 +349,12 @@ k_bgemm_rows(const uint16_t* __restrict__ A, int K, const uint16_t* __restrict__
   }
   if (ks < ksteps) step(P0{}, ks);
   // the LDS is free: every wave has passed the k-loop's last barrier
-  store_block(acc, lds + wave * 8192, row0 + wm * 64, row_end, n0 + wn * 64, Ncols, Ncols, C, C,
-              Ncols, lane);
+  if (kSwigluGrad)
+    store_block_swiglu_grad(acc, lds + wave * 8192, row0 + wm * 64, row_end, n0 + wn * 64, Ncols,
+                            preact, C, lane);
+  else
+    store_block(acc, lds + wave * 8192, row0 + wm * 64, row_end, n0 + wn * 64, Ncols, Ncols, C, C,
+                Ncols, lane);
 }
 
 // k-grouped C_e = A_e^T B_e over the rows of expert e: A rows [row][m] (lda),
@@ -422,12 +484,17 @@ hipError_t launch_bgemm_sched(const int32_t* offsets, int E, int64_t N_cap, int3
 
 hipError_t launch_bgemm_rows(const uint16_t* A, int K, const uint16_t* B0, const uint16_t* B1,
                              int ksplit, int64_t ldb, int64_t strideB, int Ncols, int64_t N_cap,
-                             const int32_t* ws, int E, uint16_t* C, hipStream_t st) {
+                             const int32_t* ws, int E, uint16_t* C, const float* preact,
+                             hipStream_t st) {
   if (N_cap == 0) return hipGetLastError();
   const int64_t row_tiles = ceil_div(N_cap, TM) + E;  // at least the real row tiles
-  const int64_t grid = ceil_div(row_tiles * ceil_div(Ncols, TN), kXcds) * kXcds;
-  hipLaunchKernelGGL(k_bgemm_rows, dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, st, A, K,
-                     B0, B1, ksplit, ldb, strideB, Ncols, ws, E, C);
+  const dim3 grid(static_cast<unsigned>(ceil_div(row_tiles * ceil_div(Ncols, TN), kXcds) * kXcds));
+  if (preact != nullptr)
+    hipLaunchKernelGGL(k_bgemm_rows<true>, grid, dim3(kThreads), 0, st, A, K, B0, B1, ksplit, ldb,
+                       strideB, Ncols, ws, E, C, preact);
+  else
+    hipLaunchKernelGGL(k_bgemm_rows<false>, grid, dim3(kThreads), 0, st, A, K, B0, B1, ksplit, ldb,
+                       strideB, Ncols, ws, E, C, nullptr);
   return hipGetLastError();
 }
 

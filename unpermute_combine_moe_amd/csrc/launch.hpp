@@ -99,7 +99,8 @@ hipError_t launch_bgemm_sched(const int32_t* offsets, int E, int64_t N_cap, int3
                               hipStream_t st);
 hipError_t launch_bgemm_rows(const uint16_t* A, int K, const uint16_t* B0, const uint16_t* B1,
                              int ksplit, int64_t ldb, int64_t strideB, int Ncols, int64_t N_cap,
-                             const int32_t* ws, int E, uint16_t* C, hipStream_t st);
+                             const int32_t* ws, int E, uint16_t* C, const float* preact,
+                             hipStream_t st);
 hipError_t launch_bgemm_kgroup(const uint16_t* A, int64_t lda, int M, const uint16_t* B,
                                int64_t ldb, int N, const int32_t* ws, int E,
                                const uint16_t* zeros, uint16_t* C0, uint16_t* C1, int split,
@@ -109,13 +110,13 @@ hipError_t launch_grouped_gemm_swiglu_grad(const uint16_t* x, const int32_t* off
                                            int64_t N_cap, int H, int I, const uint16_t* wg,
                                            const uint16_t* wu, const uint16_t* wd,
                                            const uint16_t* h, const uint16_t* dy, uint16_t* dx,
-                                           uint16_t* dwg, uint16_t* dwu, uint16_t* dwd, void* ws,
-                                           hipStream_t st);
+                                           uint16_t* dwg, uint16_t* dwu, uint16_t* dwd,
+                                           const float* preact, void* ws, hipStream_t st);
 
 size_t gemm_workspace_bytes(int E, int64_t N_cap, int H, int I);
 hipError_t launch_grouped_gemm_swiglu(const uint16_t* x, const int32_t* offsets, int E,
                                       int64_t N_cap, int H, int I, const uint16_t* wg,
                                       const uint16_t* wu, const uint16_t* wd, uint16_t* h,
-                                      uint16_t* y, void* ws, hipStream_t st);
+                                      uint16_t* y, float* preact, void* ws, hipStream_t st);
 
 }  // namespace moe

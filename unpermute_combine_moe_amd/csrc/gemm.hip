@@ -138,7 +138,13 @@ struct EpiloguePlan {
   static constexpr int kRowsPerStore = kWave / kChunks;  // rows one wave-wide store covers
   static constexpr int kStoresPerFrag = 32 / kRowsPerStore;
   static constexpr int kStores = 2 * kStoresPerFrag;
-  static constexpr int kWaveBytes = 32 * kRowBytes;     // staging area of one wave
+  static constexpr int kWaveBytes = 32 * kRowBytes;     // staged rows of one fragment
+  // Mode 0's optional fp32 pre-activations: per fragment, the wave's 64 g
+  // columns and then its 64 u columns go through the staging area as rows of
+  // 256 B (4 rows per wave-wide store); kPreStores counts their stores per tile.
+  static constexpr int kPreStoresPerFrag = (kMode == 0) ? 2 * (32 / 4) : 0;
+  static constexpr int kPreStores = 2 * kPreStoresPerFrag;
+  static constexpr int kWaveStride = (kMode == 0) ? 32 * 256 : kWaveBytes;  // per-wave area
 };
 
 template <int kRowBytes>
@@ -190,7 +196,9 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
 
   constexpr int kOutCols = (kMode == 1) ? BN : BN / 2;
   constexpr int kStoresPerTile = EpiloguePlan<kMode>::kStores;
-  static_assert(L::kLoadsPerStage + kStoresPerTile < 64, "vmcnt field is 6 bits");
+  constexpr int kPreStores = EpiloguePlan<kMode>::kPreStores;
+  static_assert(L::kLoadsPerStage + kStoresPerTile + kPreStores < 64, "vmcnt field is 6 bits");
+  const bool keep_pre = kMode == 0 && preact != nullptr;
   const int col_tiles = (Ncols + kOutCols - 1) / kOutCols;
   const int row_tiles = prefix[E];
   const int total = row_tiles * col_tiles;  // < 2^31: at most (2^31 / 128 + 1024) * 32
@@ -419,6 +427,9 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
             const bool next_loads = issued + (loads_now ? 1 : 0) > s + 2;
             if (epi_step != s - 1) {
               if (next_loads) wait_vmcnt<L::kLoadsPerStage>(); else wait_vmcnt<0>();
+            } else if (keep_pre) {
+              if (next_loads) wait_vmcnt<L::kLoadsPerStage + kStoresPerTile + kPreStores>();
+              else wait_vmcnt<kStoresPerTile + kPreStores>();
             } else {
               if (next_loads) wait_vmcnt<L::kLoadsPerStage + kStoresPerTile>();
               else wait_vmcnt<kStoresPerTile>();
@@ -455,13 +466,14 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
     epi_step = s - 1;
     {
       using EP = EpiloguePlan<kMode>;
-      static_assert(4 * EP::kWaveBytes <= kStageBytes, "staging fits one ring stage");
+      static_assert(L::kThreads / kWave * EP::kWaveStride <= kStageBytes,
+                    "staging fits one ring stage");
       // Staging space: the ring stage of step s - 1, which every wave has
       // finished reading (the barrier of that step's last sub-step, taken on
       // the workgroup's last step too) and which is refilled only by stage
       // s + 2's loads, issued during step s after the barrier at the end of
       // this epilogue.
-      lds_u8_t* stg = lds + ((cbuf + kStages - 1) % kStages) * kStageBytes + wave * EP::kWaveBytes;
+      lds_u8_t* stg = lds + ((cbuf + kStages - 1) % kStages) * kStageBytes + wave * EP::kWaveStride;
       constexpr int ldc = (kMode == 2) ? 2 : 1;  // C row stride in units of Ncols
       // Buffer stores: a store whose offset lies past the tile's last valid
       // row is dropped by the hardware, so padding rows need no branch and
@@ -501,20 +513,6 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
                 v[k] = acc[i][jj][4 * q + k];
               }
             }
-            if (kMode == 0 && preact != nullptr && row < ci.row_end && col < Ncols) {
-              // the pre-activations for the backward: g at column col, u at
-              // Ncols + col of the fp32 [N, 2 Ncols] buffer (not counted in the
-              // vmcnt waits, which only makes those waits stricter)
-              float* dst = preact + int64_t(row) * (2 * Ncols) + col;
-              const u32x4_t gv = {__float_as_uint(acc[i][jj][4 * q]), __float_as_uint(acc[i][jj][4 * q + 1]),
-                                  __float_as_uint(acc[i][jj][4 * q + 2]), __float_as_uint(acc[i][jj][4 * q + 3])};
-              const u32x4_t uv = {__float_as_uint(acc[i][jj + EP::kOutFrags][4 * q]),
-                                  __float_as_uint(acc[i][jj + EP::kOutFrags][4 * q + 1]),
-                                  __float_as_uint(acc[i][jj + EP::kOutFrags][4 * q + 2]),
-                                  __float_as_uint(acc[i][jj + EP::kOutFrags][4 * q + 3])};
-              __builtin_nontemporal_store(gv, reinterpret_cast<u32x4_t*>(dst));
-              __builtin_nontemporal_store(uv, reinterpret_cast<u32x4_t*>(dst + Ncols));
-            }
             // chunk of these four columns in the staged row, and which half of it
             const int chunk = 4 * jj + q;
             const u32x2_t pv = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
@@ -553,6 +551,44 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
           // panels in L2); y plain, since the combine that follows reads it
           // back and finds it in the caches
           __builtin_amdgcn_raw_buffer_store_b128(val, rsrc, off, 0, kMode == 1 ? 0 : /*nt*/ 2);
+        }
+        if (kMode == 0 && keep_pre) {
+          // g, then u, of this fragment (fp32, as the SwiGLU used them) through
+          // the staging area as [32 rows][256 B], written back 4 rows x 256 B
+          // per store into preact [N, 2 Ncols] (g at col, u at Ncols + col);
+          // non-temporal, dropped past the tile's valid rows like the h stores
+          const __amdgpu_buffer_rsrc_t prs = __builtin_amdgcn_make_buffer_rsrc(
+              preact + int64_t(ci.row0) * 2 * Ncols, 0, (ci.row_end - ci.row0) * 2 * Ncols * 4,
+              0x00020000);
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            // the staging area is free: this wave's reads of it have completed
+            wait_lds_reads();
+            const int r = lane % 32;
+#pragma unroll
+            for (int jj = 0; jj < EP::kOutFrags; ++jj)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const f32x16_t& a = acc[i][jj + half * EP::kOutFrags];
+                const u32x4_t pv = {__float_as_uint(a[4 * q]), __float_as_uint(a[4 * q + 1]),
+                                    __float_as_uint(a[4 * q + 2]), __float_as_uint(a[4 * q + 3])};
+                const int chunk = 8 * jj + 2 * q + lane / 32;  // columns 4 chunk .. 4 chunk + 3
+                *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>(
+                    stg + r * 256 + stage_chunk<256>(r, chunk) * 16) = pv;
+              }
+            wait_lds_reads();
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+              const int rr = 4 * t + lane / 16, c = lane % 16;
+              const u32x4_t val = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(
+                  stg + rr * 256 + stage_chunk<256>(rr, c) * 16);
+              const int lrow = wm * 64 + i * 32 + rr;
+              const int col = wcol0 + 4 * c;
+              const bool ok = ci.row0 + lrow < ci.row_end && col < Ncols;
+              const int off = ok ? (lrow * 2 * Ncols + half * Ncols + col) * 4 : 0x80000000;
+              __builtin_amdgcn_raw_buffer_store_b128(val, prs, off, 0, /*nt*/ 2);
+            }
+          }
         }
       }
       // every wave has read its staged rows before stage s + 2's loads refill

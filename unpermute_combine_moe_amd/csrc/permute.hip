@@ -13,7 +13,8 @@
 //     among the chunk's slots with its id (a wave-level match);
 //  2. one workgroup scans the table: expert counts and offsets, and for every
 //     chunk its first row in each bucket (offsets[e] plus the counts of e in
-//     earlier chunks);
+//     earlier chunks); for tables of at most kFusedTable entries every
+//     workgroup of launch 3 does this itself instead (two launches in all);
 //  3. per token: each slot's row (that first row plus its rank in the chunk),
 //     both index maps, and the row copy.
 // No global atomics: rank assignment is deterministic.
@@ -244,14 +245,27 @@ k_route_empty(int E, int32_t* __restrict__ counts, int32_t* __restrict__ offsets
 // once and writes it to the K rows its slots landed on (16-byte vectors,
 // coalesced). The slots of the workgroup's tokens are resolved first, one
 // thread each, and their rows shared through LDS.
+//
+// kScanHere (small tables, nblk * E <= kFusedTable): pass 2 is folded in. The
+// table still holds the chunks' raw counts; every workgroup loads it into LDS
+// and scans it itself (expert totals, their exclusive scan, and for each of
+// its slots the counts of the slot's expert in earlier chunks), which costs a
+// few KB of L2 reads per workgroup instead of a launch; workgroup 0 writes the
+// counts and offsets.
 constexpr int kRowWaves = 4;
 constexpr int kRowBatch = 4;  // 16-byte chunks per lane loaded before their stores
+constexpr int kFusedTable = 4096;
+constexpr int kTableLoads = kFusedTable / (kRowWaves * kWave);  // per thread
+template <bool kScanHere>
 __global__ void __launch_bounds__(kRowWaves * kWave)
 k_permute_rows(const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, SlotMask mk,
-               int64_t T, int H, int K, int E, int64_t chunk, const int32_t* __restrict__ table,
-               const int32_t* __restrict__ offsets, int32_t* __restrict__ row_of_slot,
+               int64_t T, int H, int K, int E, int64_t chunk, int nblk,
+               const int32_t* __restrict__ table, int32_t* __restrict__ counts,
+               int32_t* __restrict__ offsets, int32_t* __restrict__ row_of_slot,
                int32_t* __restrict__ sorted_slot, uint16_t* __restrict__ permuted, int nsplit) {
   __shared__ int32_t s_rows[kRowWaves * kMaxTopK];
+  __shared__ int32_t s_tab[kScanHere ? kFusedTable : 1];
+  __shared__ int32_t s_off[kScanHere ? kMaxExpertsPermute + 1 : 1];
   const int tokens = kRowWaves / nsplit;  // tokens of this workgroup
   const int64_t t0 = int64_t(blockIdx.x) * tokens;
   const int64_t S = T * K;
@@ -274,7 +288,61 @@ k_permute_rows(const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, 
       if (c < chunks) v0[bb] = load16_nt(src + c * 8);
     }
   }
-  const int32_t N = offsets[E];
+  int32_t N;
+  if (kScanHere) {
+    // the raw count table into LDS (all loads of a thread in flight together)
+    const int n = nblk * E;
+    int32_t v[kTableLoads];
+#pragma unroll
+    for (int q = 0; q < kTableLoads; ++q) {
+      const int i = q * kRowWaves * kWave + threadIdx.x;
+      v[q] = i < n ? table[i] : 0;
+    }
+#pragma unroll
+    for (int q = 0; q < kTableLoads; ++q) {
+      const int i = q * kRowWaves * kWave + threadIdx.x;
+      if (i < n) s_tab[i] = v[q];
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += kRowWaves * kWave) {
+      int32_t sum = 0;
+      for (int c = 0; c < nblk; ++c) sum += s_tab[c * E + e];
+      s_off[e] = sum;
+    }
+    __syncthreads();
+    // exclusive scan of the expert totals by the first wave: a run of
+    // ceil(E / 64) experts per lane, then a wave prefix of the run sums
+    if (threadIdx.x < kWave) {
+      const int ln = threadIdx.x;
+      const int per = (E + kWave - 1) / kWave;
+      const int elo = std::min(E, ln * per), ehi = std::min(E, elo + per);
+      int32_t run = 0;
+      for (int e = elo; e < ehi; ++e) run += s_off[e];
+      int32_t pre = run;
+      for (int o = 1; o < kWave; o <<= 1) {
+        const int32_t u = __shfl_up(pre, o, kWave);
+        if (ln >= o) pre += u;
+      }
+      int32_t acc = pre - run;
+      for (int e = elo; e < ehi; ++e) {
+        const int32_t ce = s_off[e];
+        if (blockIdx.x == 0) {
+          counts[e] = ce;
+          offsets[e] = acc;
+        }
+        s_off[e] = acc;
+        acc += ce;
+      }
+      if (ln == kWave - 1) {
+        s_off[E] = pre;
+        if (blockIdx.x == 0) offsets[E] = pre;
+      }
+    }
+    __syncthreads();
+    N = s_off[E];
+  } else {
+    N = offsets[E];
+  }
   // one thread per slot of the workgroup's tokens
   if (static_cast<int>(threadIdx.x) < tokens * K) {
     const int64_t s = t0 * K + threadIdx.x;
@@ -283,7 +351,14 @@ k_permute_rows(const uint16_t* __restrict__ x, const int32_t* __restrict__ ids, 
       const int32_t id = ids[s];
       const int32_t local = row_of_slot[s];
       if (local >= 0 && id >= 0 && id < E && mk.active(s)) {
-        row = table[(s / chunk) * E + id] + local;
+        const int b = static_cast<int>(s / chunk);
+        if (kScanHere) {
+          int32_t first = s_off[id];  // the expert's first row, then its rows in earlier chunks
+          for (int c = 0; c < b; ++c) first += s_tab[c * E + id];
+          row = first + local;
+        } else {
+          row = table[b * E + id] + local;
+        }
         sorted_slot[row] = static_cast<int32_t>(s);
       }
       row_of_slot[s] = row;
@@ -388,13 +463,21 @@ hipError_t launch_permute(const uint16_t* x, const int32_t* ids, SlotMask mk, in
   hipLaunchKernelGGL(k_route_rank, dim3(static_cast<unsigned>(p.nblk)), dim3(kChunkThreads),
                      size_t(kChunkWaves) * E * sizeof(int32_t), st, ids, mk, S, E, p.iters, table,
                      row_of_slot);
-  hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(kScanThreads), 0, st, E, p.nblk, table, counts,
-                     offsets);
   // two waves per token when there are too few tokens for several rounds of waves
   const int nsplit = (permuted != nullptr && H / 8 >= 2 * kWave && T < kSplitBelowTokens) ? 2 : 1;
-  hipLaunchKernelGGL(k_permute_rows, dim3(static_cast<unsigned>(ceil_div(T, kRowWaves / nsplit))),
-                     dim3(kRowWaves * kWave), 0, st, x, ids, mk, T, H, K, E, p.chunk, table,
-                     offsets, row_of_slot, sorted_slot, permuted, nsplit);
+  const dim3 grid(static_cast<unsigned>(ceil_div(T, kRowWaves / nsplit)));
+  const int nblk = static_cast<int>(p.nblk);  // nblk * E <= kTableMax
+  if (p.nblk * E <= kFusedTable) {
+    hipLaunchKernelGGL(k_permute_rows<true>, grid, dim3(kRowWaves * kWave), 0, st, x, ids, mk, T,
+                       H, K, E, p.chunk, nblk, table, counts, offsets, row_of_slot, sorted_slot,
+                       permuted, nsplit);
+  } else {
+    hipLaunchKernelGGL(k_route_scan, dim3(1), dim3(kScanThreads), 0, st, E, p.nblk, table, counts,
+                       offsets);
+    hipLaunchKernelGGL(k_permute_rows<false>, grid, dim3(kRowWaves * kWave), 0, st, x, ids, mk, T,
+                       H, K, E, p.chunk, nblk, table, counts, offsets, row_of_slot, sorted_slot,
+                       permuted, nsplit);
+  }
   return hipGetLastError();
 }
 

@@ -15,11 +15,12 @@
 //    e][n] (both row-contiguous): the contraction runs over the expert's rows,
 //    its ragged tail is zero-filled, and an expert without rows gets a zero
 //    tile. Tiles go out biggest expert first.
-// Operands are staged global -> registers -> LDS through two LDS buffers. In
-// k_bgemm_rows two register sets keep each k-step's loads in flight for a whole
-// step before they are stashed (measured 453 -> 422 us for dx on the skewed
-// layer); in k_bgemm_kgroup the next k-step's loads are in flight during this
-// one's MFMAs (the two-set form measured no faster there). k-contiguous tiles sit
+// In k_bgemm_rows operands are staged global -> registers -> LDS through two
+// LDS buffers, and two register sets keep each k-step's loads in flight for a
+// whole step before they are stashed (measured 453 -> 422 us for dx on the
+// skewed layer). k_bgemm_kgroup loads straight into LDS (global_load_lds,
+// no register staging and no LDS write instructions) through a three-stage
+// ring of 32-row k-steps. k-contiguous tiles sit
 // in LDS as [row][k] with the XOR swizzle of the forward kernel and are read
 // with ds_read_b128; row-contiguous tiles sit as [k][col] and the MFMA operand
 // (8 consecutive k of one column per lane) is formed by ds_read_b64_tr_b16
@@ -46,6 +47,13 @@ constexpr int kTileBytes = kTileChunks * 16;
 constexpr int kStageBytes = 2 * kTileBytes;
 constexpr int kSchedThreads = 1024;
 constexpr int kXcds = 8;
+// k_bgemm_kgroup: k-step (rows of the contraction), direct-to-LDS loads per
+// thread per operand and stage, operand tile and stage bytes, ring depth
+constexpr int kKgTK = 32;
+constexpr int kKgLoads = TM * kKgTK / 8 / kThreads;
+constexpr int kKgTile = TM * kKgTK * 2;
+constexpr int kKgStage = 2 * kKgTile;
+constexpr int kKgStages = 3;
 
 // [row][k] tile: row r, 16-byte k-chunk kc (8 per row)
 __device__ __forceinline__ int swz_rk(int r, int kc) { return r * (TK / 8) + (kc ^ ((r >> 1) & 7)); }
@@ -360,13 +368,16 @@ k_bgemm_rows(const uint16_t* __restrict__ A, int K, const uint16_t* __restrict__
 // k-grouped C_e = A_e^T B_e over the rows of expert e: A rows [row][m] (lda),
 // B rows [row][n] (ldb); C_e is [M][N] at C0 + e * M * ldc (columns at or past
 // `split` go to C1 + e * M * ldc at column n - split). Grid: E * m-tiles *
-// n-tiles, experts taken in `order` (largest first).
-__global__ void __launch_bounds__(kThreads, 2)
+// n-tiles, experts taken in `order` (largest first). Its own k-step of kKgTK
+// rows and a ring of kKgStages direct-to-LDS stages (16 KB each), so that three
+// workgroups fit a CU: the tiles of small experts are short and latency-bound,
+// and more of them in flight is what they need.
+__global__ void __launch_bounds__(kThreads, 3)
 k_bgemm_kgroup(const uint16_t* __restrict__ A, int64_t lda, int M, const uint16_t* __restrict__ B,
                int64_t ldb, int N, const int32_t* __restrict__ ws, int E,
                const uint16_t* __restrict__ zeros, uint16_t* __restrict__ C0,
                uint16_t* __restrict__ C1, int split, int64_t ldc, int bm, int bn) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kKgStages * kKgStage];
   lds_u8_t* lds = (lds_u8_t*)smem;
   const int32_t* offs = ws + (E + 1);
   const int32_t* order = ws + 2 * (E + 1);
@@ -393,36 +404,38 @@ k_bgemm_kgroup(const uint16_t* __restrict__ A, int64_t lda, int M, const uint16_
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int wm = wave & 1, wn = wave >> 1;
 
-  // this thread's chunks: k row c / 16, column chunk c % 16 (16 threads per 256-byte row)
-  int slot[kLoads], krow[kLoads], colA[kLoads], colB[kLoads];
+  // Direct-to-LDS loads: load l fills slot c = l * 256 + wave * 64 + lane of
+  // each [k][col] operand tile, i.e. k row c / 16 and swizzled chunk c % 16,
+  // so the lane loads global column chunk (c % 16) ^ 4 (k & 3).
+  int krow[kKgLoads], colA[kKgLoads], colB[kKgLoads];
 #pragma unroll
-  for (int l = 0; l < kLoads; ++l) {
-    const int c = l * kThreads + tid;
+  for (int l = 0; l < kKgLoads; ++l) {
+    const int c = l * kThreads + wave * kWave + lane;
     krow[l] = c >> 4;
-    const int cc = c & 15;
-    slot[l] = swz_kc(krow[l], cc);
+    const int cc = (c & 15) ^ (4 * (krow[l] & 3));
     colA[l] = std::min(m0 + cc * 8, M - 8);
     colB[l] = std::min(n0 + cc * 8, N - 8);
   }
-  uint4 ra[kLoads], rb[kLoads];
-  auto load = [&](int r0) {
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+  const int ksteps = static_cast<int>(ceil_div(r_hi - r_lo, kKgTK));
+  int issued = 0;
+  auto issue = [&]() {
+    const uint32_t st = uniform(static_cast<int>(lds0 + (issued % kKgStages) * kKgStage +
+                                                 wave * kWave * 16));
+    const int r0 = r_lo + issued * kKgTK;
 #pragma unroll
-    for (int l = 0; l < kLoads; ++l) {
+    for (int l = 0; l < kKgLoads; ++l) {
       const int r = r0 + krow[l];
-      const bool in = r < r_hi;  // the ragged tail reads zeros
-      const uint16_t* pa = in ? A + int64_t(r) * lda + colA[l] : zeros;
-      const uint16_t* pb = in ? B + int64_t(r) * ldb + colB[l] : zeros;
-      ra[l] = *reinterpret_cast<const uint4*>(pa);
-      rb[l] = *reinterpret_cast<const uint4*>(pb);
+      const bool in = r < r_hi;
+      load_lds16(in ? A + int64_t(r) * lda + colA[l] : zeros, st + l * kThreads * 16);
     }
-  };
-  auto stash = [&](int buf) {
-    lds_u8_t* st = lds + buf * kStageBytes;
 #pragma unroll
-    for (int l = 0; l < kLoads; ++l) {
-      st_lds16(st, slot[l], ra[l]);
-      st_lds16(st + kTileBytes, slot[l], rb[l]);
+    for (int l = 0; l < kKgLoads; ++l) {
+      const int r = r0 + krow[l];
+      const bool in = r < r_hi;
+      load_lds16(in ? B + int64_t(r) * ldb + colB[l] : zeros, st + kKgTile + l * kThreads * 16);
     }
+    ++issued;
   };
   int offA[2][2], offB[2][2];
 #pragma unroll
@@ -436,19 +449,22 @@ k_bgemm_kgroup(const uint16_t* __restrict__ A, int64_t lda, int M, const uint16_
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  const int ksteps = static_cast<int>(ceil_div(r_hi - r_lo, TK));
-  if (ksteps > 0) {
-    load(r_lo);
-    stash(0);
-    __syncthreads();
-  }
+  // Stage i goes to buffer i % kKgStages, kKgStages - 1 stages ahead of the
+  // multiply; the waits count only this thread's loads of later stages.
+  while (issued < kKgStages - 1 && issued < ksteps) issue();
   for (int ks = 0; ks < ksteps; ++ks) {
-    const int buf = ks & 1;
-    if (ks + 1 < ksteps) load(r_lo + (ks + 1) * TK);
-    const lds_u8_t* ta = lds + buf * kStageBytes;
-    const lds_u8_t* tb = ta + kTileBytes;
+    static_assert(kKgStages == 3, "one later stage at most is in flight at a wait");
+    if (issued - ks - 1 >= 1) wait_vmcnt<2 * kKgLoads>();
+    else wait_vmcnt<0>();
+    // every wave's part of stage ks is in LDS, and every wave is done reading
+    // stage ks - 1 (its MFMAs consumed those reads), whose buffer the issue
+    // below refills
+    stage_barrier();
+    if (issued < ksteps) issue();
+    const lds_u8_t* ta = lds + (ks % kKgStages) * kKgStage;
+    const lds_u8_t* tb = ta + kKgTile;
 #pragma unroll
-    for (int kk = 0; kk < TK / 16; ++kk) {
+    for (int kk = 0; kk < kKgTK / 16; ++kk) {
       bf16x8_t fa[2], fb[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) fa[i] = read_kc(ta, offA[i], kk);
@@ -460,9 +476,10 @@ k_bgemm_kgroup(const uint16_t* __restrict__ A, int64_t lda, int M, const uint16_
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
     }
-    if (ks + 1 < ksteps) stash(buf ^ 1);
-    __syncthreads();
   }
+  // every wave is done reading the stages before the epilogue stages its output
+  wait_lds_reads();
+  stage_barrier();
   const int64_t ebase = int64_t(e) * M * ldc;
   // the LDS is free: every wave has passed the k-loop's last barrier (or, for
   // an expert without rows, never used it)

@@ -18,7 +18,7 @@
 // row. Each row's sources are counted (integer atomics: the counts do not
 // depend on the order), an exclusive scan of the counts gives each row its
 // segment of a source list, and every source index is placed in its row's
-// segment (the scan is one workgroup up to 65,536 rows, three kernels beyond).
+// segment (the scan is one workgroup up to 16,384 rows, three kernels beyond).
 // One wave per whiteboard row then writes the row once: zeros for no
 // source, the correctly rounded scaled row for one source (the common case:
 // the dispatch indices name distinct rows), and for several sources their
@@ -185,7 +185,10 @@ k_wb_block_scan(int32_t* __restrict__ cnt, int64_t G, const int32_t* __restrict_
 constexpr int kOneWaves = 16;
 constexpr int kOneRows = 64;   // 64-element rows per wave
 constexpr int kOneBatch = 16;  // rows loaded together
-constexpr int64_t kOneScanMax = int64_t(kOneWaves) * kOneRows * kWave;
+// Past 16,384 rows the three-launch scan over blocks of kScanBlock counts is
+// faster (at 65,536 rows: 125.6 against 141.2 us for the whole combine).
+constexpr int64_t kOneScanMax = 16384;
+static_assert(kOneScanMax <= int64_t(kOneWaves) * kOneRows * kWave, "one workgroup's capacity");
 __global__ void __launch_bounds__(kOneWaves * kWave)
 k_wb_scan_one(int32_t* __restrict__ cnt, int64_t G64, int32_t* __restrict__ start) {
   __shared__ int32_t wsum[kOneWaves];

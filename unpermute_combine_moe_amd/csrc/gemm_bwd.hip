@@ -6,11 +6,13 @@
 //   dx  = [dg | du] [Wg ; Wu]^T        (rows grouped by expert, like the forward)
 //   dWd = h^T dy,  [dWg | dWu] = x^T [dg | du]   (sums over each expert's rows)
 //
-// Two tile kernels share one 128 x 128 x 64 tile (256 threads as 2 x 2 waves,
-// each 64 x 64 = 2 x 2 accumulators of v_mfma_f32_32x32x16_bf16, fp32):
+// Two tile kernels share one 128 x 128 output tile (256 threads as 2 x 2 waves,
+// each 64 x 64 = 2 x 2 accumulators of v_mfma_f32_32x32x16_bf16, fp32), with
+// k-steps of 64 (k_bgemm_rows) and 32 (k_bgemm_kgroup):
 //  - k_bgemm_rows: C[rows of e, :] = A[rows of e, :] B_e^T with A [row][k] and
 //    B_e [n][k] (both k-contiguous). B may be two matrices side by side along k
-//    (Wg then Wu).
+//    (Wg then Wu). Its dh instance can instead turn the block into [dg | du]
+//    with the forward's kept pre-activations (store_block_swiglu_grad).
 //  - k_bgemm_kgroup: C_e = A_e^T B_e with A_e [rows of e][m] and B_e [rows of
 //    e][n] (both row-contiguous): the contraction runs over the expert's rows,
 //    its ragged tail is zero-filled, and an expert without rows gets a zero
@@ -20,9 +22,9 @@
 // whole step before they are stashed (measured 453 -> 422 us for dx on the
 // skewed layer). k_bgemm_kgroup loads straight into LDS (global_load_lds,
 // no register staging and no LDS write instructions) through a three-stage
-// ring of 32-row k-steps. k-contiguous tiles sit
-// in LDS as [row][k] with the XOR swizzle of the forward kernel and are read
-// with ds_read_b128; row-contiguous tiles sit as [k][col] and the MFMA operand
+// ring of 32-row k-steps. k-contiguous tiles sit in LDS as [row][k] with the
+// XOR swizzle of the forward kernel and are read with ds_read_b128;
+// row-contiguous tiles sit as [k][col] and the MFMA operand
 // (8 consecutive k of one column per lane) is formed by ds_read_b64_tr_b16
 // transpose reads, as the forward kernel does for its weights.
 #include <type_traits>

@@ -268,6 +268,31 @@ def gemm_grad_ops(args, d, n_rows):
     return ops
 
 
+def graph_step_op(args, d, n_tokens):
+    """The layer step captured once as a HIP graph (torch.cuda.CUDAGraph) and
+    replayed: the same kernels without per-launch host work."""
+    import torch
+
+    permute, gemm, combine, grad = step_calls(d)
+
+    def step():
+        permute(); gemm(); combine(); grad()
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    us, usmin = time_op(g.replay, args.op_iters, None)
+    e = op_entry("layer_step_graph_replay", us, usmin)
+    e["tokens_per_s"] = round(n_tokens / (us * 1e-6), 1)
+    return e
+
+
 def run_layer(args, dev):
     import torch
 
@@ -594,6 +619,8 @@ def main():
     ops = layer_ops
     if not args.no_ops:
         ops += [dict(workload=c["name"], **o) for o in gemm_grad_ops(args, d, n_rows)]
+        ops.append(dict(workload=c["name"], timing="graph replays, caches warm",
+                        **graph_step_op(args, d, T)))
         ops = ops + run_ops(args, dev, flush)
         del flush
     cpu = None

@@ -268,9 +268,11 @@ def gemm_grad_ops(args, d, n_rows):
     return ops
 
 
-def graph_step_op(args, d, n_tokens):
+def graph_step_ops(args, d, n_tokens):
     """The layer step captured once as a HIP graph (torch.cuda.CUDAGraph) and
-    replayed: the same kernels without per-launch host work."""
+    replayed, beside the eager step timed the same way (one step between two
+    events, synchronised after each): the same kernels without per-launch host
+    work."""
     import torch
 
     permute, gemm, combine, grad = step_calls(d)
@@ -287,10 +289,13 @@ def graph_step_op(args, d, n_tokens):
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         step()
-    us, usmin = time_op(g.replay, args.op_iters, None)
-    e = op_entry("layer_step_graph_replay", us, usmin)
-    e["tokens_per_s"] = round(n_tokens / (us * 1e-6), 1)
-    return e
+    out = []
+    for name, fn in (("layer_step_eager", step), ("layer_step_graph_replay", g.replay)):
+        us, usmin = time_op(fn, args.op_iters, None)
+        e = op_entry(name, us, usmin)
+        e["tokens_per_s"] = round(n_tokens / (us * 1e-6), 1)
+        out.append(e)
+    return out
 
 
 def run_layer(args, dev):
@@ -348,6 +353,22 @@ def run_ops(args, dev, flush):
     e1 = op_entry("full_path_forward", us, usmin, flops=gemm_flops(T * K, H, I))
     e1["tokens_per_s"] = round(T / (us * 1e-6), 1)
     ops.append(dict(workload=c["name"], timing="three calls, caches warm", **e1))
+    # the same three calls captured once as a HIP graph: launch-bound work without
+    # the per-launch host cost
+    s1 = torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s1):
+        f_c1()
+    torch.cuda.current_stream().wait_stream(s1)
+    torch.cuda.synchronize()
+    g1 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g1):
+        f_c1()
+    us, usmin = time_op(g1.replay, args.op_iters, None, warm=5)
+    e1 = op_entry("full_path_forward_graph_replay", us, usmin, flops=gemm_flops(T * K, H, I))
+    e1["tokens_per_s"] = round(T / (us * 1e-6), 1)
+    ops.append(dict(workload=c["name"], timing="graph replays, caches warm", **e1))
+    del g1
     del x1, p1, h1, y1, out1
     # permute / combine, T=4096 H=2048 E=64 K=6
     g = W.gen_c2()
@@ -619,8 +640,8 @@ def main():
     ops = layer_ops
     if not args.no_ops:
         ops += [dict(workload=c["name"], **o) for o in gemm_grad_ops(args, d, n_rows)]
-        ops.append(dict(workload=c["name"], timing="graph replays, caches warm",
-                        **graph_step_op(args, d, T)))
+        ops += [dict(workload=c["name"], timing="one step per timing, caches warm", **o)
+                for o in graph_step_ops(args, d, T)]
         ops = ops + run_ops(args, dev, flush)
         del flush
     cpu = None

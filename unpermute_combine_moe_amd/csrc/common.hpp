@@ -149,6 +149,31 @@ __device__ __forceinline__ void load_lds16(const void* gptr, uint32_t lds_base) 
                : "memory", "m0");
 }
 
+// Raw buffer resource (gfx9 layout: base address, stride 0, num_records bytes,
+// the same dword 3 the compiler's make_buffer_rsrc takes); every word made
+// wave-uniform so the descriptor lives in SGPRs.
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4_t buffer_rsrc(const void* base, uint32_t num_records) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4_t r;
+  r.x = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(static_cast<uint32_t>(a)));
+  r.y = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(static_cast<uint32_t>(a >> 32) & 0xFFFFu));
+  r.z = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(num_records));
+  r.w = 0x00020000;
+  return r;
+}
+
+// 16-byte direct buffer -> LDS load: this lane's 16 bytes (at byte voffset of
+// the resource) land at LDS byte address lds_base + 16 * lane. An offset past
+// the resource's num_records is out of range: the load moves no data but is
+// issued and counted like any other, so the vmcnt bookkeeping is unchanged.
+__device__ __forceinline__ void buffer_load_lds16(i32x4_t rsrc, uint32_t voffset, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_base), "v"(voffset), "s"(rsrc)
+               : "memory", "m0");
+}
+
 // Workgroup barrier without a memory fence (a fence would also wait for the
 // loads still in flight); the "memory" clobber keeps the compiler from moving
 // LDS accesses across it.

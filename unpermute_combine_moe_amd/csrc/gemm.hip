@@ -272,17 +272,23 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
   int lj = 0;
   int lk = 0;
   int lbuf = 0;
-  const uint16_t* a_src[L::kLoadsA];
+  // A rows through a buffer resource that spans the tile's valid rows only: a
+  // padding row (a tile past the end of its expert's rows) gets an offset past
+  // the range, so its loads are issued and counted but move no data; what they
+  // leave in LDS only reaches output rows that are never stored.
+  uint32_t a_off[L::kLoadsA];
+  i32x4_t a_rsrc;
   const uint16_t* b_src[L::kLoadsB];
   auto load_tile_sources = [&](int j) {
     const TileInfo t = tile_info(j);
+    const int rows = t.row_end - t.row0;
+    a_rsrc = buffer_rsrc(A + int64_t(t.row0) * Kdim, static_cast<uint32_t>(rows * Kdim * 2));
 #pragma unroll
     for (int i = 0; i < L::kLoadsA; ++i) {
       const int slot = i * L::kThreads + wave * kWave + lane;
       const int m = slot >> 3;
       const int kc = (slot & 7) ^ ((m >> 1) & 7);
-      const int r = std::min(t.row0 + m, t.row_end - 1);
-      a_src[i] = A + int64_t(r) * Kdim + kc * 8;
+      a_off[i] = m < rows ? static_cast<uint32_t>((m * Kdim + kc * 8) * 2) : 0x80000000u;
     }
 #pragma unroll
     for (int i = 0; i < L::kLoadsB; ++i) {
@@ -310,7 +316,7 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
   // load i (0 .. kLoadsPerStage - 1) of the stage being issued
   auto load1 = [&](int i) {
     if (i < L::kLoadsA)
-      load_lds16(a_src[i] + lk * BK, l_st + i * L::kThreads * 16);
+      buffer_load_lds16(a_rsrc, a_off[i] + lk * BK * 2, l_st + i * L::kThreads * 16);
     else
       load_lds16(b_src[i - L::kLoadsA] + int64_t(lk) * BK * Ncols,
                  l_st + (kChunksA + (i - L::kLoadsA) * L::kThreads) * 16);

@@ -275,8 +275,14 @@ k_bgemm_rows(const uint16_t* __restrict__ A, int K, const uint16_t* __restrict__
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int wm = wave & 1, wn = wave >> 1;
 
-  // this thread's chunks: tile row c / 8, k-chunk c % 8 (8 threads per 128-byte row)
-  const uint16_t* a_src[kLoads];
+  // this thread's chunks: tile row c / 8, k-chunk c % 8 (8 threads per 128-byte row).
+  // A rows through a buffer resource that spans the tile's valid rows only: a
+  // padding row gets an offset past the range and loads zeros without moving
+  // any data (its output row is never stored).
+  const int rows = uniform(row_end - row0);
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(A + int64_t(uniform(row0)) * K), 0, rows * K * 2, 0x00020000);
+  uint32_t a_off[kLoads];
   int64_t b_row[kLoads];
   int slot[kLoads];
 #pragma unroll
@@ -284,7 +290,7 @@ k_bgemm_rows(const uint16_t* __restrict__ A, int K, const uint16_t* __restrict__
     const int c = l * kThreads + tid;
     const int r = c >> 3, kc = c & 7;
     slot[l] = swz_rk(r, kc);
-    a_src[l] = A + int64_t(std::min(row0 + r, row_end - 1)) * K + kc * 8;
+    a_off[l] = r < rows ? static_cast<uint32_t>((r * K + kc * 8) * 2) : 0x80000000u;
     b_row[l] = int64_t(e) * strideB + int64_t(std::min(n0 + r, Ncols - 1)) * ldb + kc * 8;
   }
   // two register sets (see the k-loop below)
@@ -296,7 +302,8 @@ k_bgemm_rows(const uint16_t* __restrict__ A, int K, const uint16_t* __restrict__
     const int kb = k0 < ksplit ? k0 : k0 - ksplit;
 #pragma unroll
     for (int l = 0; l < kLoads; ++l) {
-      ra[p][l] = *reinterpret_cast<const uint4*>(a_src[l] + k0);
+      const u32x4_t va = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_off[l] + k0 * 2, 0, 0);
+      ra[p][l] = make_uint4(va.x, va.y, va.z, va.w);
       rb[p][l] = *reinterpret_cast<const uint4*>(bb + b_row[l] + kb);
     }
   };

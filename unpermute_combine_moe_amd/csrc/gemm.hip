@@ -23,7 +23,9 @@
 // same lane and register.
 //
 // Data path: both operand tiles go from global memory straight into LDS
-// (global_load_lds_dwordx4, 16 bytes per lane, no register staging) through a
+// (16 bytes per lane, no register staging: buffer_load_dwordx4 ... lds for the
+// A rows, bounded by the tile's valid rows, global_load_lds_dwordx4 for the
+// weights) through a
 // three-stage ring, so two k-steps of loads are in flight while one is
 // multiplied; one s_barrier per k-step, with explicit vmcnt waits. A is kept
 // [row][k] and read with ds_read_b128. The weights stay in their [k][n]

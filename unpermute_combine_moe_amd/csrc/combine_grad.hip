@@ -17,6 +17,8 @@
 //    one wave per (segment, 512-wide hidden tile, group of 4 const experts).
 //  - k_const_grad_reduce / k_alpha_grad_reduce: add the segment partials in a
 //    fixed order. No atomics: the result does not depend on scheduling.
+// For per-token alpha and K <= 8 the first two run as one launch
+// (k_combine_grad_with_partials), the partial sums beside the per-token work.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -34,20 +36,19 @@ enum SlotKind : int { kDrop = 0, kRow = 1, kCopy = 2, kConst = 3 };
 // kMaxK: the slot arrays are sized for K <= kMaxK (8 or 16), so that the
 // common K <= 8 keeps half the registers; there the kernel is held to four
 // waves per SIMD (at most 128 VGPRs, which it fits without spilling).
+// The per-token body, for workgroup `block` of the per-token grid.
 template <bool kHasRowMap, bool kAlphaPerH, int kMaxK>
-__global__ void __launch_bounds__(kWaves * kWave)
-__attribute__((amdgpu_waves_per_eu(kMaxK <= 8 ? 4 : 1)))
-k_combine_grad(const uint16_t* __restrict__ grad_out, const uint16_t* __restrict__ expert_out,
-               int64_t N, const int32_t* __restrict__ row_of_slot,
-               const int32_t* __restrict__ row_map, const int32_t* __restrict__ ids,
-               const float* __restrict__ probs, SlotMask mk, int64_t T, int K, int H, int E,
-               SpecialArgs sp, CombineGradArgs o, int alpha_token, int nsplit) {
+__device__ __forceinline__ void combine_grad_tokens(
+    int block, const uint16_t* __restrict__ grad_out, const uint16_t* __restrict__ expert_out,
+    int64_t N, const int32_t* __restrict__ row_of_slot, const int32_t* __restrict__ row_map,
+    const int32_t* __restrict__ ids, const float* __restrict__ probs, SlotMask mk, int64_t T,
+    int K, int H, int E, SpecialArgs sp, CombineGradArgs o, int alpha_token, int nsplit) {
   // nsplit waves (1, 2 or 4) share a token, each taking every nsplit-th
   // 64-chunk row of the hidden dim; their per-slot sums meet in LDS
   __shared__ float xch[kWaves][2][kMaxK];
   const int w = threadIdx.x / kWave;
   const int part = w % nsplit;
-  const int64_t t = uniform(static_cast<int>(blockIdx.x * (kWaves / nsplit) + w / nsplit));
+  const int64_t t = uniform(static_cast<int>(block * (kWaves / nsplit) + w / nsplit));
   const bool live = t < T;
   if (nsplit == 1 && !live) return;
   const int lane = threadIdx.x % kWave;
@@ -222,6 +223,19 @@ k_combine_grad(const uint16_t* __restrict__ grad_out, const uint16_t* __restrict
   }
 }
 
+template <bool kHasRowMap, bool kAlphaPerH, int kMaxK>
+__global__ void __launch_bounds__(kWaves * kWave)
+__attribute__((amdgpu_waves_per_eu(kMaxK <= 8 ? 4 : 1)))
+k_combine_grad(const uint16_t* __restrict__ grad_out, const uint16_t* __restrict__ expert_out,
+               int64_t N, const int32_t* __restrict__ row_of_slot,
+               const int32_t* __restrict__ row_map, const int32_t* __restrict__ ids,
+               const float* __restrict__ probs, SlotMask mk, int64_t T, int K, int H, int E,
+               SpecialArgs sp, CombineGradArgs o, int alpha_token, int nsplit) {
+  combine_grad_tokens<kHasRowMap, kAlphaPerH, kMaxK>(
+      static_cast<int>(blockIdx.x), grad_out, expert_out, N, row_of_slot, row_map, ids, probs, mk,
+      T, K, H, E, sp, o, alpha_token, nsplit);
+}
+
 struct Partials {
   float* cv;  // [nseg][num_const][H]: sum of p * alpha2 * g
   float* a1;  // [nseg][num_const][H]: sum of p * g * ori_x   (kSharedAlpha only)
@@ -241,21 +255,22 @@ constexpr int batch_slots() { return kSharedAlpha ? 4 : 8; }
 // const group into an LDS list (wave-private), then walks the list in
 // batches whose grad_out (and ori_x, const_v, alpha) loads are all in flight
 // together.
+// The partial-sum body, for workgroup (bx, by, bz) of the partial-sum grid.
 template <bool kAlphaPerH, bool kSharedAlpha>
-__global__ void __launch_bounds__(kWaves * kWave)
-k_const_grad_partial(const uint16_t* __restrict__ grad_out, const int32_t* __restrict__ ids,
-                     const float* __restrict__ probs, SlotMask mk, int64_t T, int K, int H, int E,
-                     SpecialArgs sp, Partials part) {
+__device__ __forceinline__ void const_grad_partial_block(
+    int bx, int by, int bz, const uint16_t* __restrict__ grad_out,
+    const int32_t* __restrict__ ids, const float* __restrict__ probs, SlotMask mk, int64_t T,
+    int K, int H, int E, SpecialArgs sp, Partials part) {
   constexpr int kB = batch_slots<kSharedAlpha>();
   __shared__ int s_ent[kWaves][kRoundSlots];
   __shared__ float s_p[kWaves][kRoundSlots];
   const int w = threadIdx.x / kWave;
-  const int seg = uniform(static_cast<int>(blockIdx.y * kWaves + w));
+  const int seg = uniform(static_cast<int>(by * kWaves + w));
   if (seg >= part.nseg) return;
   const int lane = threadIdx.x % kWave;
-  const int h0 = (static_cast<int>(blockIdx.x) * kWave + lane) * 8;
+  const int h0 = (bx * kWave + lane) * 8;
   const bool hin = h0 < H;
-  const int c0 = static_cast<int>(blockIdx.z) * kConstGroup;
+  const int c0 = bz * kConstGroup;
   const int64_t const_lo = int64_t(E) + sp.num_zero + sp.num_copy;
   const int64_t t_lo = int64_t(seg) * part.seg_len;
   const int64_t t_hi = t_lo + part.seg_len < T ? t_lo + part.seg_len : T;
@@ -378,6 +393,40 @@ k_const_grad_partial(const uint16_t* __restrict__ grad_out, const int32_t* __res
       d2[1] = make_float4(aa2[q][4], aa2[q][5], aa2[q][6], aa2[q][7]);
     }
   }
+}
+
+template <bool kAlphaPerH, bool kSharedAlpha>
+__global__ void __launch_bounds__(kWaves * kWave)
+k_const_grad_partial(const uint16_t* __restrict__ grad_out, const int32_t* __restrict__ ids,
+                     const float* __restrict__ probs, SlotMask mk, int64_t T, int K, int H, int E,
+                     SpecialArgs sp, Partials part) {
+  const_grad_partial_block<kAlphaPerH, kSharedAlpha>(
+      static_cast<int>(blockIdx.x), static_cast<int>(blockIdx.y), static_cast<int>(blockIdx.z),
+      grad_out, ids, probs, mk, T, K, H, E, sp, part);
+}
+
+// One launch, two roles, for the layout whose two bodies fit the same register
+// budget (per-token alpha, K <= 8): the first n_part workgroups compute the
+// const-expert partial sums (grid px x py x pz, flattened), the others the
+// per-token gradients. The partial sums depend only on the inputs, so they
+// run beside the per-token work instead of after it.
+template <bool kHasRowMap>
+__global__ void __launch_bounds__(kWaves * kWave) __attribute__((amdgpu_waves_per_eu(4)))
+k_combine_grad_with_partials(const uint16_t* __restrict__ grad_out,
+                             const uint16_t* __restrict__ expert_out, int64_t N,
+                             const int32_t* __restrict__ row_of_slot,
+                             const int32_t* __restrict__ row_map, const int32_t* __restrict__ ids,
+                             const float* __restrict__ probs, SlotMask mk, int64_t T, int K,
+                             int H, int E, SpecialArgs sp, CombineGradArgs o, int alpha_token,
+                             int nsplit, Partials part, int px, int py, int n_part) {
+  const int b = static_cast<int>(blockIdx.x);
+  if (b < n_part)
+    const_grad_partial_block<false, false>(b % px, (b / px) % py, b / (px * py), grad_out, ids,
+                                           probs, mk, T, K, H, E, sp, part);
+  else
+    combine_grad_tokens<kHasRowMap, false, 8>(b - n_part, grad_out, expert_out, N, row_of_slot,
+                                              row_map, ids, probs, mk, T, K, H, E, sp, o,
+                                              alpha_token, nsplit);
 }
 
 __device__ __forceinline__ void add4(float4& a, const float4& b) {
@@ -548,19 +597,45 @@ hipError_t launch_combine_grad(const uint16_t* grad_out, const uint16_t* expert_
   const bool want_alpha = o.d_alpha1 != nullptr || o.d_alpha2 != nullptr;
   const bool per_h = sp.num_const > 0 && sp.a_sh != 0;
   const int alpha_token = want_alpha && lay == AlphaLayout::kPerToken;
-  {
-    // four (or two) waves per token once a token's row is long and there are
-    // too few tokens to keep every SIMD busy for several rounds
-    const int nsplit = T >= 2 * kSplitBelowTokens ? 1
-                       : H / 8 >= 4 * kWave       ? 4
-                       : H / 8 >= 2 * kWave       ? 2
-                                                  : 1;
-    const dim3 grid(static_cast<unsigned>(ceil_div(T, kWaves / nsplit)));
-    const dim3 block(kWaves * kWave);
-#define MOE_CGRAD(RM, PH, MK)                                                                  \
-  hipLaunchKernelGGL((k_combine_grad<RM, PH, MK>), grid, block, 0, st, grad_out, expert_out, N, \
-                     row_of_slot, row_map, ids, probs, mk, T, K, H, E, sp, o, alpha_token,    \
-                     nsplit)
+  const bool shared_alpha =
+      want_alpha && (lay == AlphaLayout::kSharedAlongH || lay == AlphaLayout::kSharedScalar);
+  const bool need_part = sp.num_const > 0 && (o.d_const_v != nullptr || shared_alpha);
+  // four (or two) waves per token once a token's row is long and there are
+  // too few tokens to keep every SIMD busy for several rounds
+  const int nsplit = T >= 2 * kSplitBelowTokens ? 1
+                     : H / 8 >= 4 * kWave       ? 4
+                     : H / 8 >= 2 * kWave       ? 2
+                                                : 1;
+  const int64_t main_blocks = ceil_div(T, kWaves / nsplit);
+  const dim3 block(kWaves * kWave);
+  Partials part{};
+  int px = 0, py = 0, pz = 0;
+  if (need_part) {
+    const SegPlan sg = seg_plan(T, K);
+    const size_t slab =
+        align256(size_t(sg.nseg) * size_t(sp.num_const) * size_t(H) * sizeof(float));
+    char* base = static_cast<char*>(ws);
+    part = Partials{reinterpret_cast<float*>(base), reinterpret_cast<float*>(base + slab),
+                    reinterpret_cast<float*>(base + 2 * slab), sg.nseg, sg.seg_len};
+    px = static_cast<int>(ceil_div(H, kTileH));
+    py = static_cast<int>(ceil_div(sg.nseg, kWaves));
+    pz = static_cast<int>(ceil_div(sp.num_const, kConstGroup));
+  }
+  if (need_part && !per_h && !shared_alpha && K <= 8) {
+    // the partial sums and the per-token work in one launch
+    const int n_part = px * py * pz;
+    const dim3 grid(static_cast<unsigned>(n_part + main_blocks));
+    if (row_map != nullptr)
+      hipLaunchKernelGGL(k_combine_grad_with_partials<true>, grid, block, 0, st, grad_out,
+                         expert_out, N, row_of_slot, row_map, ids, probs, mk, T, K, H, E, sp, o,
+                         alpha_token, nsplit, part, px, py, n_part);
+    else
+      hipLaunchKernelGGL(k_combine_grad_with_partials<false>, grid, block, 0, st, grad_out,
+                         expert_out, N, row_of_slot, row_map, ids, probs, mk, T, K, H, E, sp, o,
+                         alpha_token, nsplit, part, px, py, n_part);
+  } else {
+    const dim3 grid(static_cast<unsigned>(main_blocks));
+#define MOE_CGRAD(RM, PH, MK)                                                                    hipLaunchKernelGGL((k_combine_grad<RM, PH, MK>), grid, block, 0, st, grad_out, expert_out, N,                      row_of_slot, row_map, ids, probs, mk, T, K, H, E, sp, o, alpha_token,                         nsplit)
 #define MOE_CGRAD_K(RM, PH) \
   if (K <= 8) MOE_CGRAD(RM, PH, 8); else MOE_CGRAD(RM, PH, 16);
     if (row_map != nullptr) {
@@ -570,29 +645,22 @@ hipError_t launch_combine_grad(const uint16_t* grad_out, const uint16_t* expert_
     }
 #undef MOE_CGRAD_K
 #undef MOE_CGRAD
-  }
-  const bool shared_alpha =
-      want_alpha && (lay == AlphaLayout::kSharedAlongH || lay == AlphaLayout::kSharedScalar);
-  if (sp.num_const <= 0 || (o.d_const_v == nullptr && !shared_alpha)) return hipGetLastError();
-
-  const SegPlan sg = seg_plan(T, K);
-  const size_t slab = align256(size_t(sg.nseg) * size_t(sp.num_const) * size_t(H) * sizeof(float));
-  char* base = static_cast<char*>(ws);
-  const Partials part{reinterpret_cast<float*>(base), reinterpret_cast<float*>(base + slab),
-                      reinterpret_cast<float*>(base + 2 * slab), sg.nseg, sg.seg_len};
-  const dim3 grid(static_cast<unsigned>(ceil_div(H, kTileH)),
-                  static_cast<unsigned>(ceil_div(sg.nseg, kWaves)),
-                  static_cast<unsigned>(ceil_div(sp.num_const, kConstGroup)));
-  const dim3 block(kWaves * kWave);
-#define MOE_CPART(PH, SA)                                                                       \
-  hipLaunchKernelGGL((k_const_grad_partial<PH, SA>), grid, block, 0, st, grad_out, ids, probs, \
+    if (need_part) {
+      const dim3 pgrid(static_cast<unsigned>(px), static_cast<unsigned>(py),
+                       static_cast<unsigned>(pz));
+#define MOE_CPART(PH, SA)                                                                   \
+  hipLaunchKernelGGL((k_const_grad_partial<PH, SA>), pgrid, block, 0, st, grad_out, ids, probs, \
                      mk, T, K, H, E, sp, part)
-  if (per_h) {
-    if (shared_alpha) MOE_CPART(true, true); else MOE_CPART(true, false);
-  } else {
-    if (shared_alpha) MOE_CPART(false, true); else MOE_CPART(false, false);
-  }
+      if (per_h) {
+        if (shared_alpha) MOE_CPART(true, true); else MOE_CPART(true, false);
+      } else {
+        if (shared_alpha) MOE_CPART(false, true); else MOE_CPART(false, false);
+      }
 #undef MOE_CPART
+    }
+  }
+  if (!need_part) return hipGetLastError();
+
   const int64_t n4 = int64_t(sp.num_const) * H / 4;
   hipLaunchKernelGGL(k_const_grad_reduce, dim3(static_cast<unsigned>(ceil_div(n4, kRedCols))),
                      dim3(kWaves * kWave), 0, st, part, sp.num_const, H, sp.a_sc, o.d_const_v,

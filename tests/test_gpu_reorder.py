@@ -26,7 +26,7 @@ def _run(moe, x, counts, R, El, N=None, rows=True):
 
 @pytest.mark.parametrize("R,El,N,H,seed", [
     (1, 1, 1, 8, 0), (1, 9, 500, 16, 1), (6, 1, 333, 24, 2), (8, 32, 4000, 136, 3),
-    (3, 5, 0, 8, 4), (16, 64, 20000, 8, 5), (256, 256, 70000, 8, 6),
+    (3, 5, 0, 8, 4), (16, 64, 20000, 8, 5), (5, 205, 3000, 8, 7), (256, 256, 70000, 8, 6),
 ])
 def test_reorder_random(moe_lib, R, El, N, H, seed):
     counts = W.make_rank_major_counts(R, El, N, seed)

@@ -6,7 +6,8 @@
 // row of destination row i.
 //
 // One workgroup builds the block tables (two exclusive scans over R*E_local
-// entries); the row kernel then gives each workgroup a run of destination
+// entries; for at most 1024 blocks every row workgroup does it itself instead);
+// the row kernel then gives each workgroup a run of destination
 // rows: one thread per row finds its block by binary search over the
 // destination block starts, and the four waves copy the rows as 16-byte
 // vectors.
@@ -59,14 +60,46 @@ k_reorder_setup(const int32_t* __restrict__ counts, int R, int El, int32_t* __re
   }
 }
 
+// kScanHere (at most kFusedBlocks blocks): no setup launch; every workgroup
+// loads the block counts into LDS and runs the two scans itself (a few KB of
+// L2 reads per workgroup instead of a launch), and workgroup 0 writes the
+// per-expert counts and offsets.
+constexpr int kFusedBlocks = 1024;
+template <bool kScanHere>
 __global__ void __launch_bounds__(kRowThreads)
-k_reorder_rows(const uint16_t* __restrict__ x, const int32_t* __restrict__ ws, int B, int64_t N,
-               int H, uint16_t* __restrict__ y, int32_t* __restrict__ perm,
-               int32_t* __restrict__ inv_perm) {
+k_reorder_rows(const uint16_t* __restrict__ x, const int32_t* __restrict__ counts, int R, int El,
+               const int32_t* __restrict__ ws, int B, int64_t N, int H, uint16_t* __restrict__ y,
+               int32_t* __restrict__ perm, int32_t* __restrict__ inv_perm,
+               int32_t* __restrict__ tokens_per_expert, int32_t* __restrict__ offsets) {
   __shared__ int32_t src_of[kRowsPerWg];
+  __shared__ int32_t s_src[kScanHere ? kFusedBlocks : 1];  // rank-major block starts
+  __shared__ int32_t s_dst[kScanHere ? kFusedBlocks : 1];  // expert-major block starts
+  __shared__ int32_t s_part[kScanHere ? kRowThreads : 1];
+  int64_t total;
+  if (kScanHere) {
+    // block counts (negative counts read as 0): s_src in (r, e) order, s_dst in (e, r) order
+    for (int i = threadIdx.x; i < B; i += kRowThreads) {
+      const int e = i / R, r = i % R;
+      s_src[i] = std::max(counts[i], 0);
+      s_dst[i] = std::max(counts[r * El + e], 0);
+    }
+    __syncthreads();
+    block_exclusive_scan<kRowThreads>(s_src, s_src, B, s_part);
+    total = block_exclusive_scan<kRowThreads>(s_dst, s_dst, B, s_part);
+    if (blockIdx.x == 0) {
+      for (int e = threadIdx.x; e < El; e += kRowThreads) {
+        const int32_t start = s_dst[e * R];
+        const int32_t end = (e + 1 < El) ? s_dst[(e + 1) * R] : static_cast<int32_t>(total);
+        offsets[e] = start;
+        tokens_per_expert[e] = end - start;
+      }
+      if (threadIdx.x == 0) offsets[El] = static_cast<int32_t>(total);
+    }
+  } else {
+    total = ws[4 * B];
+  }
   const int32_t* src_em = ws + 2 * B;
-  const int32_t* dst_em = ws + 3 * B;
-  const int64_t total = ws[4 * B];
+  const int32_t* dst_em = kScanHere ? s_dst : ws + 3 * B;
   const int64_t i0 = int64_t(blockIdx.x) * kRowsPerWg;
   if (threadIdx.x < kRowsPerWg) {
     const int64_t i = i0 + threadIdx.x;
@@ -79,7 +112,9 @@ k_reorder_rows(const uint16_t* __restrict__ x, const int32_t* __restrict__ ws, i
         const int mid = (lo + hi) >> 1;
         if (dst_em[mid] <= i) lo = mid; else hi = mid;
       }
-      const int64_t s = int64_t(src_em[lo]) + (i - dst_em[lo]);
+      // the source start of block (e, r) = lo: rank-major block r * El + e
+      const int64_t sstart = kScanHere ? s_src[(lo % R) * El + lo / R] : src_em[lo];
+      const int64_t s = sstart + (i - dst_em[lo]);
       src = (s >= 0 && s < N) ? static_cast<int32_t>(s) : -1;
     }
     if (i < N) {
@@ -131,11 +166,18 @@ hipError_t launch_reorder(const uint16_t* x, const int32_t* counts, int R, int E
                           int H, uint16_t* y, int32_t* perm, int32_t* inv_perm,
                           int32_t* tokens_per_expert, int32_t* offsets, void* ws, hipStream_t st) {
   int32_t* w = static_cast<int32_t*>(ws);
+  const int B = R * E_local;
+  const dim3 grid(static_cast<unsigned>(ceil_div(N, kRowsPerWg)));
+  if (N > 0 && B <= kFusedBlocks) {
+    hipLaunchKernelGGL(k_reorder_rows<true>, grid, dim3(kRowThreads), 0, st, x, counts, R,
+                       E_local, w, B, N, H, y, perm, inv_perm, tokens_per_expert, offsets);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(k_reorder_setup, dim3(1), dim3(kSetupThreads), 0, st, counts, R, E_local, w,
                      tokens_per_expert, offsets);
   if (N > 0) {
-    hipLaunchKernelGGL(k_reorder_rows, dim3(static_cast<unsigned>(ceil_div(N, kRowsPerWg))),
-                       dim3(kRowThreads), 0, st, x, w, R * E_local, N, H, y, perm, inv_perm);
+    hipLaunchKernelGGL(k_reorder_rows<false>, grid, dim3(kRowThreads), 0, st, x, counts, R,
+                       E_local, w, B, N, H, y, perm, inv_perm, tokens_per_expert, offsets);
   }
   return hipGetLastError();
 }

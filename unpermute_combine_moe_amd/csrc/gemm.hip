@@ -171,6 +171,28 @@ __device__ __forceinline__ bf16x8_t lds_read_a(const lds_u8_t* base, int slot) {
 // kMode 2: gate/up recomputed for the backward; with dh = aux [N, Ncols], the
 // epilogue writes C [N, 2 * Ncols] = [dg | du], dg = dh * u * s (1 + g (1 - s)),
 // du = dh * g * s, s = 1 / (1 + exp(-g)) (the SwiGLU derivative).
+// Direct-to-LDS loads of the k-loop with the fewest instructions. The A rows
+// take the k-step offset in the buffer's scalar offset (the lane offset stays
+// the tile's); each B source pointer advances one k-step in place, and that
+// add also covers the wait state m0 needs before an LDS-DMA load. (m0 is set
+// with s_mov: an add into m0 would write SCC, and an SCC clobber lets the
+// compiler move the MFMAs out of the issue order the k-loop pins.)
+__device__ __forceinline__ void buffer_load_lds16_at(i32x4_t rsrc, uint32_t voffset,
+                                                     uint32_t soffset, uint32_t lds_base,
+                                                     int off) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds_base + off), "v"(voffset), "s"(rsrc), "s"(soffset)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void global_load_lds16_step(const uint16_t*& p, uint64_t adv,
+                                                       uint32_t lds_base, int off) {
+  asm volatile("s_mov_b32 m0, %1\n\tv_lshl_add_u64 %0, %2, 0, %0\n\tglobal_load_lds_dwordx4 %0, off"
+               : "+v"(p)
+               : "s"(lds_base + off), "s"(adv)
+               : "memory", "m0");
+}
+
 template <int kMode>
 __global__ void __launch_bounds__(Layout<kMode>::kThreads, 1)
 k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0,
@@ -238,7 +260,7 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
   // loads run two steps ahead of the multiply across tile boundaries, so the
   // next tile's first stages are in flight during this tile's epilogue.
   const int first = t_lo + static_cast<int>(blockIdx.x) / kXcds;
-  const int ntiles = (first < t_hi) ? (t_hi - 1 - first) / per_xcd + 1 : 0;
+  const int ntiles = uniform((first < t_hi) ? (t_hi - 1 - first) / per_xcd + 1 : 0);
   const int nsteps = ntiles * ksteps;
 
   struct TileInfo {
@@ -280,7 +302,10 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
   // leave in LDS only reaches output rows that are never stored.
   uint32_t a_off[L::kLoadsA];
   i32x4_t a_rsrc;
+  // B sources one k-step before the next load's (each load first advances
+  // its pointer by one k-step of rows)
   const uint16_t* b_src[L::kLoadsB];
+  const uint64_t b_adv = uint64_t(BK) * Ncols * 2;
   auto load_tile_sources = [&](int j) {
     const TileInfo t = tile_info(j);
     const int rows = t.row_end - t.row0;
@@ -307,7 +332,7 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
         col = t.n0 + c * 8;
       }
       if (col >= Ncols) col = 0;  // columns past the matrix: any valid address, never stored
-      b_src[i] = base + int64_t(t.e) * Kdim * Ncols + int64_t(k) * Ncols + col;
+      b_src[i] = base + int64_t(t.e) * Kdim * Ncols + int64_t(k - BK) * Ncols + col;
     }
   };
   uint32_t l_st = 0;
@@ -318,10 +343,10 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
   // load i (0 .. kLoadsPerStage - 1) of the stage being issued
   auto load1 = [&](int i) {
     if (i < L::kLoadsA)
-      buffer_load_lds16(a_rsrc, a_off[i] + lk * BK * 2, l_st + i * L::kThreads * 16);
+      buffer_load_lds16_at(a_rsrc, a_off[i], uniform(lk * BK * 2), l_st, i * L::kThreads * 16);
     else
-      load_lds16(b_src[i - L::kLoadsA] + int64_t(lk) * BK * Ncols,
-                 l_st + (kChunksA + (i - L::kLoadsA) * L::kThreads) * 16);
+      global_load_lds16_step(b_src[i - L::kLoadsA], b_adv, l_st,
+                             (kChunksA + (i - L::kLoadsA) * L::kThreads) * 16);
   };
   auto issue_end = [&]() {
     lbuf = (lbuf + 1 == kStages) ? 0 : lbuf + 1;
@@ -389,10 +414,12 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
       acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[c][jj], fa[c][i], acc[i][jj], 0, 0, 0);
     };
 
-    for (int kstep = 0; kstep < ksteps; ++kstep, ++s) {
+    // One k-step; kLoads (stage s + 2 goes out during this step) is a
+    // template constant so the steady-state body carries no per-load branch.
+    auto kstep_body = [&](auto loads_tag) {
+      constexpr bool loads_now = decltype(loads_tag)::value;
       const lds_u8_t* st = lds + cbuf * kStageBytes;
       cbuf = (cbuf + 1 == kStages) ? 0 : cbuf + 1;
-      const bool loads_now = issued < nsteps;  // stage s + 2 goes out during this step
       const bool more = s + 1 < nsteps;
       if (loads_now) issue_begin();
       // One MFMA, then up to two LDS reads or one load: the non-MFMA
@@ -432,7 +459,9 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
           __builtin_amdgcn_sched_barrier(0);
           wait_lds_reads();  // on every path: this wave is done reading stage s
           if (more) {
-            const bool next_loads = issued + (loads_now ? 1 : 0) > s + 2;
+            // stage s + 2 is in flight: issued now, or earlier (never, once the
+            // loads have run out)
+            const bool next_loads = loads_now || issued > s + 2;
             if (epi_step != s - 1) {
               if (next_loads) wait_vmcnt<L::kLoadsPerStage>(); else wait_vmcnt<0>();
             } else if (keep_pre) {
@@ -469,7 +498,13 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
         issue_end();
         ++issued;
       }
-    }
+    };
+    // k-step s issues stage s + 2 while s + 2 < nsteps: in this tile the
+    // first kload steps do, the rest (the workgroup's last two) do not
+    const int kload = std::min(ksteps, std::max(0, nsteps - 2 - j * ksteps));
+    int kstep = 0;
+    for (; kstep < kload; ++kstep, ++s) kstep_body(std::true_type{});
+    for (; kstep < ksteps; ++kstep, ++s) kstep_body(std::false_type{});
 
     epi_step = s - 1;
     {

@@ -27,7 +27,10 @@
 // A rows, bounded by the tile's valid rows, global_load_lds_dwordx4 for the
 // weights) through a
 // three-stage ring, so two k-steps of loads are in flight while one is
-// multiplied; one s_barrier per k-step, with explicit vmcnt waits. A is kept
+// multiplied; one s_barrier per k-step, with explicit vmcnt waits. Every
+// k-step but a workgroup's last two issues the loads of the step two ahead;
+// those run as a loop of their own so the steady-state body has no per-load
+// branch. A is kept
 // [row][k] and read with ds_read_b128. The weights stay in their [k][n]
 // layout in LDS and the MFMA B operand (8 consecutive k of one column per
 // lane) is formed by two ds_read_b64_tr_b16 transpose reads: within each group
@@ -166,11 +169,6 @@ __device__ __forceinline__ bf16x8_t lds_read_a(const lds_u8_t* base, int slot) {
   return r;
 }
 
-// kMode 0: gate/up + SwiGLU -> h.  kMode 1: down -> y.
-// kMode 0 with preact != nullptr also stores g and u (fp32) as preact [N, 2 Ncols].
-// kMode 2: gate/up recomputed for the backward; with dh = aux [N, Ncols], the
-// epilogue writes C [N, 2 * Ncols] = [dg | du], dg = dh * u * s (1 + g (1 - s)),
-// du = dh * g * s, s = 1 / (1 + exp(-g)) (the SwiGLU derivative).
 // Direct-to-LDS loads of the k-loop with the fewest instructions. The A rows
 // take the k-step offset in the buffer's scalar offset (the lane offset stays
 // the tile's); each B source pointer advances one k-step in place, and that
@@ -193,6 +191,11 @@ __device__ __forceinline__ void global_load_lds16_step(const uint16_t*& p, uint6
                : "memory", "m0");
 }
 
+// kMode 0: gate/up + SwiGLU -> h.  kMode 1: down -> y.
+// kMode 0 with preact != nullptr also stores g and u (fp32) as preact [N, 2 Ncols].
+// kMode 2: gate/up recomputed for the backward; with dh = aux [N, Ncols], the
+// epilogue writes C [N, 2 * Ncols] = [dg | du], dg = dh * u * s (1 + g (1 - s)),
+// du = dh * g * s, s = 1 / (1 + exp(-g)) (the SwiGLU derivative).
 template <int kMode>
 __global__ void __launch_bounds__(Layout<kMode>::kThreads, 1)
 k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0,

@@ -79,6 +79,30 @@ def test_gemm_many_experts(moe_lib):
     assert_h_within_ulp(hb[:n], h_ref)
 
 
+@pytest.mark.parametrize("H,I,rows_per_expert,seed", [
+    (64, 64, 12_345, 41),    # one k-step per tile in both passes
+    (128, 128, 6_001, 42),   # two k-steps per tile
+])
+def test_gemm_many_tiles_short_k(moe_lib, H, I, rows_per_expert, seed):
+    # several tiles per workgroup with tiles of one or two k-steps: the loads
+    # that run ahead cross tile boundaries and a workgroup's two load-free
+    # k-steps fall into different tiles
+    rng = np.random.default_rng(seed)
+    counts = [rows_per_expert] * 7 + [rows_per_expert // 3]
+    E = len(counts)
+    off = _offsets(counts)
+    N = int(off[-1]) + 7
+    x = W.normal_bf16(rng, (N, H))
+    wg = W.normal_bf16(rng, (E, H, I), 0.02)
+    wu = W.normal_bf16(rng, (E, H, I), 0.02)
+    wd = W.normal_bf16(rng, (E, I, H), 0.02)
+    hb, yb = _gemm(moe_lib, x, off, wg, wu, wd)
+    n = int(off[-1])
+    h_ref, y_ref = oracle.grouped_swiglu(x[:n], off, wg, wu, wd)
+    assert np.max(np.abs(f64(yb[:n]) - y_ref)) <= gemm_tol(H)
+    assert_h_within_ulp(hb[:n], h_ref)
+
+
 def test_gemm_config1(moe_lib):
     g = W.gen_c1()
     c = g["cfg"]

@@ -178,9 +178,14 @@ __device__ __forceinline__ bf16x8_t lds_read_a(const lds_u8_t* base, int slot) {
 __device__ __forceinline__ void buffer_load_lds16_at(i32x4_t rsrc, uint32_t voffset,
                                                      uint32_t soffset, uint32_t lds_base,
                                                      int off) {
+  // the descriptor words made wave-uniform again here (free when they already
+  // are), so the "s" operand never lands in VGPRs whatever the caller's code
+  i32x4_t r;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) r[w] = __builtin_amdgcn_readfirstlane(rsrc[w]);
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
-               : "s"(lds_base + off), "v"(voffset), "s"(rsrc), "s"(soffset)
+               : "s"(lds_base + off), "v"(voffset), "s"(r), "s"(soffset)
                : "memory", "m0");
 }
 __device__ __forceinline__ void global_load_lds16_step(const uint16_t*& p, uint64_t adv,

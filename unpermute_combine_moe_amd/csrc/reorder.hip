@@ -18,7 +18,7 @@ namespace moe {
 namespace {
 
 constexpr int kSetupThreads = 1024;
-constexpr int kRowsPerWg = 32;
+constexpr int kRowsPerWg = 16;
 constexpr int kRowThreads = 256;
 constexpr int kCopyBatch = 8;  // 16-byte chunks per lane in flight in the row copy
 

@@ -5,6 +5,10 @@
 // goes through one grouped matmul plus SwiGLU instead of a per-expert loop.
 //   pass 1 (gate/up):  h = bf16( silu(x Wg[e]) * (x Wu[e]) )   fp32 accumulate
 //   pass 2 (down):     y = bf16( h Wd[e] )                      fp32 accumulate
+// The same kernel runs the backward's row-grouped products: the gate/up
+// recompute with the SwiGLU derivative, dh = dy Wd[e]^T (optionally turned
+// straight into [dg | du] with kept pre-activations) and dx = [dg | du]
+// [Wg[e] ; Wu[e]]^T, whose B operands are stored [n][k].
 //
 // Work decomposition. A small scheduling kernel turns the device-side expert
 // offsets into a row-tile prefix (ceil(rows_e / BM) tiles per expert, 0 for an
@@ -111,12 +115,13 @@ constexpr int kStages = 3;
 constexpr int kStageBytes = (kChunksA + kChunksB) * 16;
 
 // Waves of a workgroup: 2 (64-row halves) x kWavesN (B-column blocks). The
-// gate/up passes use 4 waves (one per SIMD, 64 x 128 each); the down pass,
-// whose tiles are only 8 k-steps long, uses 8 (two per SIMD, 64 x 64 each),
-// measured faster there (217 against 227 us) and not for gate/up.
+// gate/up passes and the backward's dh use 4 waves (one per SIMD, 64 x 128
+// each); the down pass, whose tiles are only 8 k-steps long, uses 8 (two per
+// SIMD, 64 x 64 each), measured faster there (217 against 227 us) and not for
+// gate/up; the backward's plain row GEMM (dx) uses 8 as well.
 template <int kMode>
 struct Layout {
-  static constexpr int kWavesN = (kMode == 1) ? 4 : 2;
+  static constexpr int kWavesN = (kMode == 1 || kMode == 3) ? 4 : 2;
   static constexpr int kThreads = 2 * kWavesN * kWave;
   static constexpr int kColFrags = BN / 32 / kWavesN;     // 32-column MFMA blocks per wave
   static constexpr int kLoadsA = kChunksA / kThreads;     // direct-to-LDS loads per thread per stage
@@ -124,6 +129,15 @@ struct Layout {
   static constexpr int kLoadsPerStage = kLoadsA + kLoadsB;
   static constexpr int kReads = 2 + 2 * kColFrags;        // LDS fragment reads per sub-step
   static constexpr int kMfmas = 2 * kColFrags;            // MFMAs per sub-step
+};
+// kPaired: the tile's 256 B-columns are 128 gate and the matching 128 up
+// columns (gate/up passes); otherwise 256 plain output columns. kBkc: B_e is
+// stored [n][k] (k contiguous, the backward's dh and dx), loaded and read like
+// the A rows; otherwise [k][n], read with transpose reads.
+template <int kMode>
+struct Mode {
+  static constexpr bool kPaired = kMode == 0 || kMode == 2;
+  static constexpr bool kBkc = kMode == 3 || kMode == 4;
 };
 // Epilogue. Each 32-row fragment of a wave's output goes through LDS: the
 // lanes write their MFMA results (one token row per lane, four consecutive
@@ -137,12 +151,13 @@ struct Layout {
 template <int kMode>
 struct EpiloguePlan {
   static constexpr int kOutFrags =
-      (kMode == 1) ? Layout<kMode>::kColFrags : Layout<kMode>::kColFrags / 2;
+      Mode<kMode>::kPaired ? Layout<kMode>::kColFrags / 2 : Layout<kMode>::kColFrags;
   static constexpr int kRowBytes = kOutFrags * 64 * (kMode == 2 ? 2 : 1);
   static constexpr int kChunks = kRowBytes / 16;        // per staged row
   static constexpr int kRowsPerStore = kWave / kChunks;  // rows one wave-wide store covers
   static constexpr int kStoresPerFrag = 32 / kRowsPerStore;
-  static constexpr int kStores = 2 * kStoresPerFrag;
+  // mode 4 writes dg and du for every staged chunk of dh
+  static constexpr int kStores = (kMode == 4 ? 4 : 2) * kStoresPerFrag;
   static constexpr int kWaveBytes = 32 * kRowBytes;     // staged rows of one fragment
   // Mode 0's optional fp32 pre-activations: per fragment, the wave's 64 g
   // columns and then its 64 u columns go through the staging area as rows of
@@ -201,11 +216,17 @@ __device__ __forceinline__ void global_load_lds16_step(const uint16_t*& p, uint6
 // kMode 2: gate/up recomputed for the backward; with dh = aux [N, Ncols], the
 // epilogue writes C [N, 2 * Ncols] = [dg | du], dg = dh * u * s (1 + g (1 - s)),
 // du = dh * g * s, s = 1 / (1 + exp(-g)) (the SwiGLU derivative).
+// kMode 3: C = A B_e^T with B_e = [B0[e] | B1[e]] stored [n][k] (B0 holding
+// k < ksplit, B1 the rest; dx of the backward, and dh without kept
+// pre-activations). kMode 4: the dh GEMM (B_e = Wd[e] stored [n][k]) whose
+// epilogue rounds dh to bf16 and forms C [N, 2 * Ncols] = [dg | du] from the
+// kept pre-activations preact [N, 2 Ncols] (read only).
 template <int kMode>
 __global__ void __launch_bounds__(Layout<kMode>::kThreads, 1)
 k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0,
        const uint16_t* __restrict__ B1, int Ncols, const int32_t* __restrict__ ws, int E,
-       uint16_t* __restrict__ C, const uint16_t* __restrict__ aux, float* __restrict__ preact) {
+       uint16_t* __restrict__ C, const uint16_t* __restrict__ aux, float* __restrict__ preact,
+       int ksplit) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes];
   // row-tile prefix and clamped expert offsets, staged once per workgroup so the
   // per-tile expert lookup is a binary search in LDS
@@ -226,7 +247,8 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
   const int wm = wave & 1;   // 64-row half of the tile
   const int wn = wave >> 1;  // B-column block
 
-  constexpr int kOutCols = (kMode == 1) ? BN : BN / 2;
+  using MD = Mode<kMode>;
+  constexpr int kOutCols = MD::kPaired ? BN / 2 : BN;
   constexpr int kStoresPerTile = EpiloguePlan<kMode>::kStores;
   constexpr int kPreStores = EpiloguePlan<kMode>::kPreStores;
   static_assert(L::kLoadsPerStage + kStoresPerTile + kPreStores < 64, "vmcnt field is 6 bits");
@@ -253,7 +275,7 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
     // matching up columns
     constexpr int kHalf = L::kColFrags / 2;
     int ncol;
-    if (kMode != 1) ncol = (j < kHalf ? 0 : BN / 2) + wn * (BN / 2 / L::kWavesN) + (j % kHalf) * 32;
+    if (MD::kPaired) ncol = (j < kHalf ? 0 : BN / 2) + wn * (BN / 2 / L::kWavesN) + (j % kHalf) * 32;
     else ncol = wn * (BN / L::kWavesN) + j * 32;
     const int n = ncol + 16 * (g16 % 2) + 4 * (i16 % 4);
 #pragma unroll
@@ -313,7 +335,7 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
   // B sources one k-step before the next load's (each load first advances
   // its pointer by one k-step of rows)
   const uint16_t* b_src[L::kLoadsB];
-  const uint64_t b_adv = uint64_t(BK) * Ncols * 2;
+  const uint64_t b_adv = MD::kBkc ? uint64_t(BK) * 2 : uint64_t(BK) * Ncols * 2;
   auto load_tile_sources = [&](int j) {
     const TileInfo t = tile_info(j);
     const int rows = t.row_end - t.row0;
@@ -328,11 +350,20 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
 #pragma unroll
     for (int i = 0; i < L::kLoadsB; ++i) {
       const int slot = i * L::kThreads + wave * kWave + lane;
+      if (MD::kBkc) {
+        // B_e rows n (k contiguous, ksplit per row in B0), stored like the A rows
+        const int n = slot >> 3;
+        const int kc = (slot & 7) ^ ((n >> 1) & 7);
+        int ng = t.n0 + n;
+        if (ng >= Ncols) ng = 0;  // rows past the matrix: any valid address, never stored
+        b_src[i] = B0 + (int64_t(t.e) * Ncols + ng) * ksplit + kc * 8 - BK;
+        continue;
+      }
       const int k = slot >> 5;
       const int c = (slot & 31) ^ (4 * (k & 3));
       const uint16_t* base;
       int col;
-      if (kMode != 1) {
+      if (MD::kPaired) {
         base = (c < 16) ? B0 : B1;
         col = t.n0 + (c % 16) * 8;
       } else {
@@ -344,8 +375,16 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
     }
   };
   uint32_t l_st = 0;
+  // kBkc: at the k-step where k reaches ksplit the B sources move from B0[e] to
+  // the same rows of B1[e] (ksplit is a multiple of BK)
+  const int lk_b1 = MD::kBkc ? ksplit / BK : -1;
   auto issue_begin = [&]() {
-    if (lk == 0) load_tile_sources(lj);
+    if (lk == 0) {
+      load_tile_sources(lj);
+    } else if (MD::kBkc && lk == lk_b1) {
+#pragma unroll
+      for (int i = 0; i < L::kLoadsB; ++i) b_src[i] = B1 + ((b_src[i] - B0) - ksplit);
+    }
     l_st = uniform(static_cast<int>(lds0 + lbuf * kStageBytes + wave * kWave * 16));
   };
   // load i (0 .. kLoadsPerStage - 1) of the stage being issued
@@ -379,9 +418,16 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
       na[i] = lds_read_a(st_, swz(wm * 64 + i * 32 + lane % 32, kk_ * 2 + lane / 32));
     } else {
       const int jj = (r - 1) / 2, half = (r - 1) % 2;
-      const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (lds_v4i16_t*)(st_ + b_off[jj][half] + kk_ * 16 * (BN * 2)));
-      __builtin_memcpy(reinterpret_cast<char*>(&nb[jj]) + 8 * half, &v, 8);
+      if (MD::kBkc) {
+        // rows n of B_e, k-chunk kk * 2 + lane / 32: read like the A rows
+        if (half == 0)
+          nb[jj] = lds_read_a(st_ + kChunksA * 16,
+                              swz(wn * (BN / L::kWavesN) + jj * 32 + lane % 32, kk_ * 2 + lane / 32));
+      } else {
+        const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_v4i16_t*)(st_ + b_off[jj][half] + kk_ * 16 * (BN * 2)));
+        __builtin_memcpy(reinterpret_cast<char*>(&nb[jj]) + 8 * half, &v, 8);
+      }
     }
   };
   // Schedule of one k-step (one wave per SIMD, in-order issue: a wave issues
@@ -525,14 +571,14 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
       // s + 2's loads, issued during step s after the barrier at the end of
       // this epilogue.
       lds_u8_t* stg = lds + ((cbuf + kStages - 1) % kStages) * kStageBytes + wave * EP::kWaveStride;
-      constexpr int ldc = (kMode == 2) ? 2 : 1;  // C row stride in units of Ncols
+      constexpr int ldc = (kMode == 2 || kMode == 4) ? 2 : 1;  // C row stride in units of Ncols
       // Buffer stores: a store whose offset lies past the tile's last valid
       // row is dropped by the hardware, so padding rows need no branch and
       // every lane issues every store (the vmcnt waits count them).
       const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
           C + int64_t(ci.row0) * Ncols * ldc, 0, (ci.row_end - ci.row0) * Ncols * ldc * 2,
           0x00020000);
-      const int wcol0 = ci.n0 + ((kMode == 1) ? wn * (BN / L::kWavesN) : wn * (BN / 2 / L::kWavesN));  // wave's first output column
+      const int wcol0 = ci.n0 + (MD::kPaired ? wn * (BN / 2 / L::kWavesN) : wn * (BN / L::kWavesN));  // wave's first output column
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int r = lane % 32;  // this lane's row in the fragment
@@ -588,6 +634,39 @@ k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0
           const u32x4_t val = *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(
               stg + rr * EP::kRowBytes + stage_chunk<EP::kRowBytes>(rr, c) * 16);
           const int lrow = wm * 64 + i * 32 + rr;  // row within the tile
+          if (kMode == 4) {
+            // eight bf16 dh values of one row: dg and du from the kept
+            // pre-activations, each written as one 16-byte store
+            const int col = wcol0 + c * 8;
+            const bool ok = ci.row0 + lrow < ci.row_end && col < Ncols;
+            u32x4_t dgv = {0u, 0u, 0u, 0u}, duv = {0u, 0u, 0u, 0u};
+            if (ok) {
+              const float* pg = preact + int64_t(ci.row0 + lrow) * (2 * Ncols) + col;
+              const u32x4_t g0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(pg));
+              const u32x4_t g1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(pg + 4));
+              const u32x4_t u0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(pg + Ncols));
+              const u32x4_t u1 =
+                  __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(pg + Ncols + 4));
+              const uint32_t gw[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+              const uint32_t uw[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+              const uint32_t dw[4] = {val.x, val.y, val.z, val.w};
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                float dg0, du0, dg1, du1;
+                swiglu_grad(bf16_lo(dw[q]), __uint_as_float(gw[2 * q]), __uint_as_float(uw[2 * q]),
+                            &dg0, &du0);
+                swiglu_grad(bf16_hi(dw[q]), __uint_as_float(gw[2 * q + 1]),
+                            __uint_as_float(uw[2 * q + 1]), &dg1, &du1);
+                dgv[q] = pack_bf16x2(dg0, dg1);
+                duv[q] = pack_bf16x2(du0, du1);
+              }
+            }
+            const int off = ok ? (lrow * 2 * Ncols + col) * 2 : 0x80000000;
+            const int off2 = ok ? (lrow * 2 * Ncols + Ncols + col) * 2 : 0x80000000;
+            __builtin_amdgcn_raw_buffer_store_b128(dgv, rsrc, off, 0, /*nt*/ 2);
+            __builtin_amdgcn_raw_buffer_store_b128(duv, rsrc, off2, 0, /*nt*/ 2);
+            continue;
+          }
           int col, dst_col;
           if (kMode == 2) {
             col = wcol0 + (c % (EP::kChunks / 2)) * 8;
@@ -676,9 +755,9 @@ hipError_t launch_grouped_gemm_swiglu(const uint16_t* x, const int32_t* offsets,
   if (N_cap == 0) return hipGetLastError();
   const int G = persistent_grid();
   hipLaunchKernelGGL(k_gemm<0>, dim3(G), dim3(Layout<0>::kThreads), 0, st, x, H, wg, wu, I, w, E,
-                     h, nullptr, preact);
+                     h, nullptr, preact, 0);
   hipLaunchKernelGGL(k_gemm<1>, dim3(G), dim3(Layout<1>::kThreads), 0, st, h, I, wd, nullptr, H, w,
-                     E, y, nullptr, nullptr);
+                     E, y, nullptr, nullptr, 0);
   return hipGetLastError();
 }
 
@@ -727,29 +806,27 @@ hipError_t launch_grouped_gemm_swiglu_grad(const uint16_t* x, const int32_t* off
   uint16_t* dh = reinterpret_cast<uint16_t*>(base + off_dh);
   uint16_t* dgu = reinterpret_cast<uint16_t*>(base + off_dgu);
   hipLaunchKernelGGL(k_fill_zero, dim3(1), dim3(64), 0, st, reinterpret_cast<uint32_t*>(zeros), 64);
-  if (preact == nullptr)
-    hipLaunchKernelGGL(k_gemm_sched, dim3(1), dim3(kSchedThreads), 0, st, offsets, E, N_cap, w);
+  hipLaunchKernelGGL(k_gemm_sched, dim3(1), dim3(kSchedThreads), 0, st, offsets, E, N_cap, w);
   hipError_t err = launch_bgemm_sched(offsets, E, N_cap, bt, st);
   if (err != hipSuccess) return err;
   if (N_cap > 0) {
+    const int G = persistent_grid();
     if (preact != nullptr) {
-      // [dg | du] straight from the dh GEMM (dy Wd^T, B_e = Wd[e] as [I][H])
-      err = launch_bgemm_rows(dy, H, wd, wd, H, H, int64_t(I) * H, I, N_cap, bt, E, dgu, preact,
-                              st);
-      if (err != hipSuccess) return err;
+      // [dg | du] straight from the dh GEMM (dy Wd^T, B_e = Wd[e] stored [I][H])
+      hipLaunchKernelGGL(k_gemm<4>, dim3(G), dim3(Layout<4>::kThreads), 0, st, dy, H, wd, wd, I,
+                         w, E, dgu, nullptr, const_cast<float*>(preact), H);
     } else {
-      // dh = dy Wd^T: B_e = Wd[e] as [I][H]
-      err = launch_bgemm_rows(dy, H, wd, wd, H, H, int64_t(I) * H, I, N_cap, bt, E, dh, nullptr,
-                              st);
-      if (err != hipSuccess) return err;
-      // [dg | du] from the recomputed gate and up tiles
-      const int G = persistent_grid();
+      // dh = dy Wd^T (B_e = Wd[e] stored [I][H]), then [dg | du] from the
+      // recomputed gate and up tiles
+      hipLaunchKernelGGL(k_gemm<3>, dim3(G), dim3(Layout<3>::kThreads), 0, st, dy, H, wd, wd, I,
+                         w, E, dh, nullptr, nullptr, H);
       hipLaunchKernelGGL(k_gemm<2>, dim3(G), dim3(Layout<2>::kThreads), 0, st, x, H, wg, wu, I, w,
-                         E, dgu, dh, nullptr);
+                         E, dgu, dh, nullptr, 0);
     }
-    // dx = [dg | du] [Wg ; Wu]^T: B_e = Wg[e], Wu[e] as [H][I] side by side along k
-    err = launch_bgemm_rows(dgu, 2 * I, wg, wu, I, I, int64_t(H) * I, H, N_cap, bt, E, dx, nullptr,
-                            st);
+    // dx = [dg | du] [Wg ; Wu]^T: B_e = Wg[e], Wu[e] stored [H][I], side by side along k
+    hipLaunchKernelGGL(k_gemm<3>, dim3(G), dim3(Layout<3>::kThreads), 0, st, dgu, 2 * I, wg, wu, H,
+                       w, E, dx, nullptr, nullptr, I);
+    err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   // dWd = h^T dy  ([E, I, H]),  [dWg | dWu] = x^T [dg | du]  ([E, H, I] each)

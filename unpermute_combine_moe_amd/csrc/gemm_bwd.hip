@@ -1,32 +1,23 @@
-// Grouped GEMMs of the SwiGLU expert FFN backward (gfx950 bf16 MFMA).
+// Weight-gradient GEMMs of the SwiGLU expert FFN backward (gfx950 bf16 MFMA).
 //
 // Follows the twinkle grouped-matmul PR ("feat(moe): NPU平台 EP experts forward
 // 计算改用 NPU grouped matmul"), differentiated: with dh = dy Wd^T and
 // (dg, du) from the SwiGLU derivative,
-//   dx  = [dg | du] [Wg ; Wu]^T        (rows grouped by expert, like the forward)
 //   dWd = h^T dy,  [dWg | dWu] = x^T [dg | du]   (sums over each expert's rows)
+// (the row-grouped products dh and dx = [dg | du] [Wg ; Wu]^T run on the
+// forward's grouped kernel, with B stored [n][k]).
 //
-// Two tile kernels share one 128 x 128 output tile (256 threads as 2 x 2 waves,
-// each 64 x 64 = 2 x 2 accumulators of v_mfma_f32_32x32x16_bf16, fp32), with
-// k-steps of 64 (k_bgemm_rows) and 32 (k_bgemm_kgroup):
-//  - k_bgemm_rows: C[rows of e, :] = A[rows of e, :] B_e^T with A [row][k] and
-//    B_e [n][k] (both k-contiguous). B may be two matrices side by side along k
-//    (Wg then Wu). Its dh instance can instead turn the block into [dg | du]
-//    with the forward's kept pre-activations (store_block_swiglu_grad).
-//  - k_bgemm_kgroup: C_e = A_e^T B_e with A_e [rows of e][m] and B_e [rows of
-//    e][n] (both row-contiguous): the contraction runs over the expert's rows,
-//    its ragged tail is zero-filled, and an expert without rows gets a zero
-//    tile. Tiles go out biggest expert first.
-// In k_bgemm_rows operands are staged global -> registers -> LDS through two
-// LDS buffers, and two register sets keep each k-step's loads in flight for a
-// whole step before they are stashed (measured 453 -> 422 us for dx on the
-// skewed layer). k_bgemm_kgroup loads straight into LDS (global_load_lds,
-// no register staging and no LDS write instructions) through a three-stage
-// ring of 32-row k-steps. k-contiguous tiles sit in LDS as [row][k] with the
-// XOR swizzle of the forward kernel and are read with ds_read_b128;
-// row-contiguous tiles sit as [k][col] and the MFMA operand
-// (8 consecutive k of one column per lane) is formed by ds_read_b64_tr_b16
-// transpose reads, as the forward kernel does for its weights.
+// k_bgemm_kgroup: C_e = A_e^T B_e with A_e [rows of e][m] and B_e [rows of
+// e][n] (both row-contiguous): the contraction runs over the expert's rows,
+// its ragged tail is zero-filled, and an expert without rows gets a zero
+// tile. Tiles go out biggest expert first. One 128 x 128 output tile per
+// workgroup (256 threads as 2 x 2 waves, each 64 x 64 = 2 x 2 accumulators of
+// v_mfma_f32_32x32x16_bf16, fp32); k-steps of 32 rows loaded straight into LDS
+// (global_load_lds, no register staging and no LDS write instructions)
+// through a three-stage ring. The tiles sit in LDS as [k][col] and the MFMA
+// operand (8 consecutive k of one column per lane) is formed by
+// ds_read_b64_tr_b16 transpose reads, as the forward kernel does for its
+// weights.
 #include <type_traits>
 
 #include "common.hpp"
@@ -41,12 +32,8 @@ typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
 
-constexpr int TM = 128, TN = 128, TK = 64;
+constexpr int TM = 128, TN = 128;
 constexpr int kThreads = 256;
-constexpr int kTileChunks = TM * TK / 8;             // 16-byte chunks per operand tile
-constexpr int kLoads = kTileChunks / kThreads;        // per thread per operand per step
-constexpr int kTileBytes = kTileChunks * 16;
-constexpr int kStageBytes = 2 * kTileBytes;
 constexpr int kSchedThreads = 1024;
 constexpr int kXcds = 8;
 // k_bgemm_kgroup: k-step (rows of the contraction), direct-to-LDS loads per
@@ -57,19 +44,8 @@ constexpr int kKgTile = TM * kKgTK * 2;
 constexpr int kKgStage = 2 * kKgTile;
 constexpr int kKgStages = 3;
 
-// [row][k] tile: row r, 16-byte k-chunk kc (8 per row)
-__device__ __forceinline__ int swz_rk(int r, int kc) { return r * (TK / 8) + (kc ^ ((r >> 1) & 7)); }
 // [k][col] tile: k row, 16-byte column chunk c (16 per row)
 __device__ __forceinline__ int swz_kc(int k, int c) { return k * (TM / 8) + (c ^ (4 * (k & 3))); }
-
-// MFMA operand (rows base + lane % 32, k = 16 kk + 8 (lane / 32) + 0..7) of a [row][k] tile
-__device__ __forceinline__ bf16x8_t read_rk(const lds_u8_t* t, int base, int kk, int lane) {
-  const int slot = swz_rk(base + lane % 32, kk * 2 + lane / 32);
-  const u32x4_t v = *(const __attribute__((address_space(3))) u32x4_t*)(t + slot * 16);
-  bf16x8_t r;
-  __builtin_memcpy(&r, &v, 16);
-  return r;
-}
 
 // Byte offsets of the two transpose reads that form the operand of columns
 // col0 .. col0 + 31 of a [k][col] tile at k-substep 0 (substep kk adds 16 k
@@ -92,11 +68,6 @@ __device__ __forceinline__ bf16x8_t read_kc(const lds_u8_t* t, const int off[2],
   __builtin_memcpy(&r, &lo, 8);
   __builtin_memcpy(reinterpret_cast<char*>(&r) + 8, &hi, 8);
   return r;
-}
-
-__device__ __forceinline__ void st_lds16(lds_u8_t* t, int slot, const uint4& v) {
-  const u32x4_t u = {v.x, v.y, v.z, v.w};
-  *(__attribute__((address_space(3))) u32x4_t*)(t + slot * 16) = u;
 }
 
 // Epilogue of one wave's 64 x 64 accumulator block, rows m0 .. m0 + 63 and
@@ -151,50 +122,6 @@ __device__ __forceinline__ void store_block(const f32x16_t acc[2][2], lds_u8_t* 
   }
 }
 
-// The block taken as dh (rows m, columns n < I), rounded to bf16 as a stored dh
-// would be, and turned into the SwiGLU gradients with the forward's fp32
-// pre-activations g = preact[m][n], u = preact[m][I + n]: dg goes to
-// dgu[m][n] and du to dgu[m][I + n] (bf16). dh itself is never stored.
-__device__ __forceinline__ void store_block_swiglu_grad(const f32x16_t acc[2][2], lds_u8_t* stg,
-                                                        int m0, int m_end, int n0, int I,
-                                                        const float* __restrict__ preact,
-                                                        uint16_t* __restrict__ dgu, int lane) {
-  stage_block(acc, stg, lane);
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const int r = 8 * t + lane / 8, c = lane % 8;
-    const u32x4_t v = staged_chunk(stg, r, c);
-    const int m = m0 + r, n = n0 + 8 * c;
-    if (m < m_end && n < I) {
-      const float* pg = preact + int64_t(m) * (2 * I) + n;
-      const u32x4_t g0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(pg));
-      const u32x4_t g1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(pg + 4));
-      const u32x4_t u0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(pg + I));
-      const u32x4_t u1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(pg + I + 4));
-      const float g[8] = {__uint_as_float(g0.x), __uint_as_float(g0.y), __uint_as_float(g0.z),
-                          __uint_as_float(g0.w), __uint_as_float(g1.x), __uint_as_float(g1.y),
-                          __uint_as_float(g1.z), __uint_as_float(g1.w)};
-      const float u[8] = {__uint_as_float(u0.x), __uint_as_float(u0.y), __uint_as_float(u0.z),
-                          __uint_as_float(u0.w), __uint_as_float(u1.x), __uint_as_float(u1.y),
-                          __uint_as_float(u1.z), __uint_as_float(u1.w)};
-      const uint32_t dw[4] = {v.x, v.y, v.z, v.w};
-      float dg[8], du[8];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        swiglu_grad(bf16_lo(dw[k]), g[2 * k], u[2 * k], &dg[2 * k], &du[2 * k]);
-        swiglu_grad(bf16_hi(dw[k]), g[2 * k + 1], u[2 * k + 1], &dg[2 * k + 1], &du[2 * k + 1]);
-      }
-      const u32x4_t og = {pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]),
-                          pack_bf16x2(dg[4], dg[5]), pack_bf16x2(dg[6], dg[7])};
-      const u32x4_t ou = {pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]),
-                          pack_bf16x2(du[4], du[5]), pack_bf16x2(du[6], du[7])};
-      uint16_t* dst = dgu + int64_t(m) * (2 * I) + n;
-      *reinterpret_cast<u32x4_t*>(dst) = og;
-      *reinterpret_cast<u32x4_t*>(dst + I) = ou;
-    }
-  }
-}
-
 // ws layout (int32): prefix[E+1] | offs[E+1] | order[E]
 //   prefix: row-tile prefix (ceil(rows_e / TM) per expert), offs: clamped
 //   offsets, order: experts by row count, largest first (ties: lower id first).
@@ -234,144 +161,6 @@ k_bgemm_sched(const int32_t* __restrict__ offsets, int E, int64_t N_cap, int32_t
     for (int o = 0; o < E; ++o) rank += (rows[o] > mine || (rows[o] == mine && o < e)) ? 1 : 0;
     order[rank] = e;
   }
-}
-
-// Row-grouped C = A B^T. A [rows][K] (lda = K), B_e = B0/B1 + e * strideB with
-// element (n, k) at n * ldb + k for k < ksplit (B0) and n * ldb + k - ksplit
-// (B1) otherwise. Grid: an upper bound of the row tiles times the column tiles.
-// kSwigluGrad: C is taken as dh and the epilogue writes [dg | du] instead
-// (store_block_swiglu_grad, with Ncols = I and C = dgu [rows, 2 I]).
-template <bool kSwigluGrad>
-__global__ void __launch_bounds__(kThreads, 2)
-k_bgemm_rows(const uint16_t* __restrict__ A, int K, const uint16_t* __restrict__ B0,
-             const uint16_t* __restrict__ B1, int ksplit, int64_t ldb, int64_t strideB, int Ncols,
-             const int32_t* __restrict__ ws, int E, uint16_t* __restrict__ C,
-             const float* __restrict__ preact) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * kStageBytes];
-  lds_u8_t* lds = (lds_u8_t*)smem;
-  const int32_t* prefix = ws;
-  const int32_t* offs = ws + (E + 1);
-  const int col_tiles = (Ncols + TN - 1) / TN;
-  // Workgroup b runs on XCD b % 8: each XCD takes a contiguous range of the
-  // row-tile-major tile list, so the column tiles of a row block (which share
-  // its A rows) and the row tiles of an expert (which share its weights) meet
-  // in one L2. The grid is a multiple of 8 and covers every real tile.
-  const int total = prefix[E] * col_tiles;
-  const int per_xcd = (total + kXcds - 1) / kXcds;
-  const int pos = static_cast<int>(blockIdx.x) / kXcds;
-  const int tile = (static_cast<int>(blockIdx.x) % kXcds) * per_xcd + pos;
-  if (pos >= per_xcd || tile >= total) return;
-  const int rt = tile / col_tiles;
-  const int ct = tile % col_tiles;
-  int lo = 0, hi = E;  // expert of row tile rt: last e with prefix[e] <= rt
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (prefix[mid] <= rt) lo = mid; else hi = mid;
-  }
-  const int e = lo;
-  const int row0 = offs[e] + (rt - prefix[e]) * TM;
-  const int row_end = std::min(row0 + TM, offs[e + 1]);
-  const int n0 = ct * TN;
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int wm = wave & 1, wn = wave >> 1;
-
-  // this thread's chunks: tile row c / 8, k-chunk c % 8 (8 threads per 128-byte row).
-  // A rows through a buffer resource that spans the tile's valid rows only: a
-  // padding row gets an offset past the range and loads zeros without moving
-  // any data (its output row is never stored).
-  const int rows = uniform(row_end - row0);
-  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(A + int64_t(uniform(row0)) * K), 0, rows * K * 2, 0x00020000);
-  uint32_t a_off[kLoads];
-  int64_t b_row[kLoads];
-  int slot[kLoads];
-#pragma unroll
-  for (int l = 0; l < kLoads; ++l) {
-    const int c = l * kThreads + tid;
-    const int r = c >> 3, kc = c & 7;
-    slot[l] = swz_rk(r, kc);
-    a_off[l] = r < rows ? static_cast<uint32_t>((r * K + kc * 8) * 2) : 0x80000000u;
-    b_row[l] = int64_t(e) * strideB + int64_t(std::min(n0 + r, Ncols - 1)) * ldb + kc * 8;
-  }
-  // two register sets (see the k-loop below)
-  uint4 ra[2][kLoads], rb[2][kLoads];
-  auto load = [&](auto P, int ks) {
-    constexpr int p = decltype(P)::value;
-    const int k0 = ks * TK;
-    const uint16_t* bb = k0 < ksplit ? B0 : B1;
-    const int kb = k0 < ksplit ? k0 : k0 - ksplit;
-#pragma unroll
-    for (int l = 0; l < kLoads; ++l) {
-      const u32x4_t va = __builtin_amdgcn_raw_buffer_load_b128(a_rsrc, a_off[l] + k0 * 2, 0, 0);
-      ra[p][l] = make_uint4(va.x, va.y, va.z, va.w);
-      rb[p][l] = *reinterpret_cast<const uint4*>(bb + b_row[l] + kb);
-    }
-  };
-  auto stash = [&](auto P, int buf) {
-    constexpr int p = decltype(P)::value;
-    lds_u8_t* st = lds + buf * kStageBytes;
-#pragma unroll
-    for (int l = 0; l < kLoads; ++l) {
-      st_lds16(st, slot[l], ra[p][l]);
-      st_lds16(st + kTileBytes, slot[l], rb[p][l]);
-    }
-  };
-  f32x16_t acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  const int ksteps = K / TK;
-  using P0 = std::integral_constant<int, 0>;
-  using P1 = std::integral_constant<int, 1>;
-  // k-step ks is multiplied from LDS buffer ks & 1; register set ks & 1 holds
-  // it between its load and its stash. A set is reloaded (two k-steps ahead)
-  // right after its stash, so its loads have a whole step to land. Stash and
-  // reload are unconditional (past the last k-step they repeat it, in bounds,
-  // and nothing reads the result), which keeps the compiler's vmcnt waits exact.
-  auto last = [&](int k) { return k < ksteps ? k : ksteps - 1; };
-  load(P0{}, 0);
-  load(P1{}, last(1));
-  stash(P0{}, 0);
-  load(P0{}, last(2));
-  __syncthreads();
-  auto step = [&](auto P, int ks) {
-    constexpr int p = decltype(P)::value;
-    using Q = std::integral_constant<int, 1 - p>;
-    const lds_u8_t* ta = lds + p * kStageBytes;
-    const lds_u8_t* tb = ta + kTileBytes;
-#pragma unroll
-    for (int kk = 0; kk < TK / 16; ++kk) {
-      bf16x8_t fa[2], fb[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) fa[i] = read_rk(ta, wm * 64 + 32 * i, kk, lane);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) fb[j] = read_rk(tb, wn * 64 + 32 * j, kk, lane);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
-    }
-    stash(Q{}, 1 - p);       // k-step ks + 1
-    load(Q{}, last(ks + 3));
-    __syncthreads();
-  };
-  int ks = 0;
-  for (; ks + 1 < ksteps; ks += 2) {
-    step(P0{}, ks);
-    step(P1{}, ks + 1);
-  }
-  if (ks < ksteps) step(P0{}, ks);
-  // the LDS is free: every wave has passed the k-loop's last barrier
-  if (kSwigluGrad)
-    store_block_swiglu_grad(acc, lds + wave * 8192, row0 + wm * 64, row_end, n0 + wn * 64, Ncols,
-                            preact, C, lane);
-  else
-    store_block(acc, lds + wave * 8192, row0 + wm * 64, row_end, n0 + wn * 64, Ncols, Ncols, C, C,
-                Ncols, lane);
 }
 
 // k-grouped C_e = A_e^T B_e over the rows of expert e: A rows [row][m] (lda),
@@ -505,22 +294,6 @@ size_t bgemm_sched_bytes(int E) {
 hipError_t launch_bgemm_sched(const int32_t* offsets, int E, int64_t N_cap, int32_t* ws,
                               hipStream_t st) {
   hipLaunchKernelGGL(k_bgemm_sched, dim3(1), dim3(kSchedThreads), 0, st, offsets, E, N_cap, ws);
-  return hipGetLastError();
-}
-
-hipError_t launch_bgemm_rows(const uint16_t* A, int K, const uint16_t* B0, const uint16_t* B1,
-                             int ksplit, int64_t ldb, int64_t strideB, int Ncols, int64_t N_cap,
-                             const int32_t* ws, int E, uint16_t* C, const float* preact,
-                             hipStream_t st) {
-  if (N_cap == 0) return hipGetLastError();
-  const int64_t row_tiles = ceil_div(N_cap, TM) + E;  // at least the real row tiles
-  const dim3 grid(static_cast<unsigned>(ceil_div(row_tiles * ceil_div(Ncols, TN), kXcds) * kXcds));
-  if (preact != nullptr)
-    hipLaunchKernelGGL(k_bgemm_rows<true>, grid, dim3(kThreads), 0, st, A, K, B0, B1, ksplit, ldb,
-                       strideB, Ncols, ws, E, C, preact);
-  else
-    hipLaunchKernelGGL(k_bgemm_rows<false>, grid, dim3(kThreads), 0, st, A, K, B0, B1, ksplit, ldb,
-                       strideB, Ncols, ws, E, C, nullptr);
   return hipGetLastError();
 }
 

@@ -97,10 +97,6 @@ int persistent_grid();
 size_t bgemm_sched_bytes(int E);
 hipError_t launch_bgemm_sched(const int32_t* offsets, int E, int64_t N_cap, int32_t* ws,
                               hipStream_t st);
-hipError_t launch_bgemm_rows(const uint16_t* A, int K, const uint16_t* B0, const uint16_t* B1,
-                             int ksplit, int64_t ldb, int64_t strideB, int Ncols, int64_t N_cap,
-                             const int32_t* ws, int E, uint16_t* C, const float* preact,
-                             hipStream_t st);
 hipError_t launch_bgemm_kgroup(const uint16_t* A, int64_t lda, int M, const uint16_t* B,
                                int64_t ldb, int N, const int32_t* ws, int E,
                                const uint16_t* zeros, uint16_t* C0, uint16_t* C1, int split,

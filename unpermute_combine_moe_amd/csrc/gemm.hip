@@ -35,15 +35,18 @@
 // k-step but a workgroup's last two issues the loads of the step two ahead;
 // those run as a loop of their own so the steady-state body has no per-load
 // branch. A is kept
-// [row][k] and read with ds_read_b128. The weights stay in their [k][n]
-// layout in LDS and the MFMA B operand (8 consecutive k of one column per
-// lane) is formed by two ds_read_b64_tr_b16 transpose reads: within each group
-// of 16 lanes, output lane 4a+b takes element b of input lanes a, a+4, a+8,
-// a+12, so input lane i points at row k0 + i/4, column 4*(i%4).
+// [row][k] and read with ds_read_b128. Weights stored [k][n] (the forward's,
+// and the recompute's) stay in that layout in LDS and the MFMA B operand (8
+// consecutive k of one column per lane) is formed by two ds_read_b64_tr_b16
+// transpose reads: within each group of 16 lanes, output lane 4a+b takes
+// element b of input lanes a, a+4, a+8, a+12, so input lane i points at row
+// k0 + i/4, column 4*(i%4). Weights stored [n][k] (the backward's dh and dx)
+// are loaded and read like the A rows.
 // Both tiles are stored in 16-byte chunks with an XOR swizzle of the chunk
-// index (A: by (row / 2) & 7, B: by 4 * (k & 3)) that keeps the operand reads free of
-// bank conflicts; the swizzle is applied by choosing which global chunk each
-// lane loads, since a direct-to-LDS load writes lane L at base + 16 L.
+// index ([row][k]: by (row / 2) & 7, [k][n]: by 4 * (k & 3)) that keeps the
+// operand reads free of bank conflicts; the swizzle is applied by choosing
+// which global chunk each lane loads, since a direct-to-LDS load writes lane L
+// at base + 16 L.
 //
 // Epilogue: the output fragments are staged in LDS (in the ring stage that the
 // tile's last k-step has just freed) and written back row-contiguous with

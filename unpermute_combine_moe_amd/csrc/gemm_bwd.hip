@@ -10,8 +10,8 @@
 // k_bgemm_kgroup: C_e = A_e^T B_e with A_e [rows of e][m] and B_e [rows of
 // e][n] (both row-contiguous): the contraction runs over the expert's rows,
 // its ragged tail is zero-filled, and an expert without rows gets a zero
-// tile. Tiles go out biggest expert first. One 128 x 128 output tile per
-// workgroup (256 threads as 2 x 2 waves, each 64 x 64 = 2 x 2 accumulators of
+// tile. Tiles go out biggest expert first. One 128 x 256 output tile per
+// workgroup (256 threads as 2 x 2 waves, each 64 x 128 = 2 x 4 accumulators of
 // v_mfma_f32_32x32x16_bf16, fp32); k-steps of 32 rows loaded straight into LDS
 // (global_load_lds, no register staging and no LDS write instructions)
 // through a three-stage ring. The tiles sit in LDS as [k][col] and the MFMA
@@ -32,66 +32,70 @@ typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
 
-constexpr int TM = 128, TN = 128;
+constexpr int TM = 128, TN = 256;
 constexpr int kThreads = 256;
 constexpr int kSchedThreads = 1024;
 constexpr int kXcds = 8;
 // k_bgemm_kgroup: k-step (rows of the contraction), direct-to-LDS loads per
 // thread per operand and stage, operand tile and stage bytes, ring depth
 constexpr int kKgTK = 32;
-constexpr int kKgLoads = TM * kKgTK / 8 / kThreads;
-constexpr int kKgTile = TM * kKgTK * 2;
-constexpr int kKgStage = 2 * kKgTile;
+constexpr int kKgLoadsA = TM * kKgTK / 8 / kThreads;
+constexpr int kKgLoadsB = TN * kKgTK / 8 / kThreads;
+constexpr int kKgTileA = TM * kKgTK * 2;
+constexpr int kKgStage = kKgTileA + TN * kKgTK * 2;
 constexpr int kKgStages = 3;
 
 // [k][col] tile: k row, 16-byte column chunk c (16 per row)
-__device__ __forceinline__ int swz_kc(int k, int c) { return k * (TM / 8) + (c ^ (4 * (k & 3))); }
+template <int W>
+__device__ __forceinline__ int swz_kc(int k, int c) { return k * (W / 8) + (c ^ (4 * (k & 3))); }
 
 // Byte offsets of the two transpose reads that form the operand of columns
 // col0 .. col0 + 31 of a [k][col] tile at k-substep 0 (substep kk adds 16 k
 // rows, which keeps k & 3 and so the swizzle): within each group of 16 lanes,
 // input lane i points at k row i / 4 (+ 4 for the second read), column 4 (i % 4).
+template <int W>
 __device__ __forceinline__ void tr_offsets(int col0, int lane, int off[2]) {
   const int g16 = lane / 16, i16 = lane % 16;
   const int n = col0 + 16 * (g16 % 2) + 4 * (i16 % 4);
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     const int k = 8 * (g16 / 2) + i16 / 4 + 4 * half;
-    off[half] = swz_kc(k, n / 8) * 16 + (n % 8) * 2;
+    off[half] = swz_kc<W>(k, n / 8) * 16 + (n % 8) * 2;
   }
 }
 
+template <int W>
 __device__ __forceinline__ bf16x8_t read_kc(const lds_u8_t* t, const int off[2], int kk) {
-  const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(t + off[0] + kk * 16 * (TM * 2)));
-  const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(t + off[1] + kk * 16 * (TM * 2)));
+  const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(t + off[0] + kk * 16 * (W * 2)));
+  const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(t + off[1] + kk * 16 * (W * 2)));
   bf16x8_t r;
   __builtin_memcpy(&r, &lo, 8);
   __builtin_memcpy(reinterpret_cast<char*>(&r) + 8, &hi, 8);
   return r;
 }
 
-// Epilogue of one wave's 64 x 64 accumulator block, rows m0 .. m0 + 63 and
-// columns n0 .. n0 + 63. In registers a lane holds row m0 + 32 i + lane % 32
+// Epilogue of one wave's 64 x 128 accumulator block, rows m0 .. m0 + 63 and
+// columns n0 .. n0 + 127. In registers a lane holds row m0 + 32 i + lane % 32
 // and four consecutive columns n0 + 32 j + 8 q + 4 (lane / 32), so a direct
-// store would cover 32 rows x 16 B. The block goes through the wave's 8 KB
-// staging area `stg` in LDS as [64 rows][128 B] of bf16 (16-byte chunks
-// XOR-swizzled by (row / 2) % 8, which keeps both the column-wise writes and
-// the row-wise reads free of bank conflicts) and is read back 16 B (8 columns)
-// per lane, 8 rows x 128 B per wave-wide access.
-__device__ __forceinline__ void stage_block(const f32x16_t acc[2][2], lds_u8_t* stg, int lane) {
+// store would cover 32 rows x 16 B. The block goes through the wave's 16 KB
+// staging area `stg` in LDS as [64 rows][256 B] of bf16 (16-byte chunks
+// XOR-swizzled by row % 16, which keeps both the column-wise writes and the
+// row-wise reads free of bank conflicts) and is read back 16 B (8 columns)
+// per lane, 4 rows x 256 B per wave-wide access.
+__device__ __forceinline__ void stage_block(const f32x16_t acc[2][4], lds_u8_t* stg, int lane) {
   typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int r = 32 * i + lane % 32;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const u32x2_t packed = {pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
                                 pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3])};
-        const int chunk = (4 * j + q) ^ ((r >> 1) & 7);
+        const int chunk = (4 * j + q) ^ (r & 15);
         *reinterpret_cast<__attribute__((address_space(3))) u32x2_t*>(
-            stg + r * 128 + chunk * 16 + (lane / 32) * 8) = packed;
+            stg + r * 256 + chunk * 16 + (lane / 32) * 8) = packed;
       }
   }
   // the wave's own writes have completed before it reads them back
@@ -101,18 +105,18 @@ __device__ __forceinline__ void stage_block(const f32x16_t acc[2][2], lds_u8_t* 
 // Staged row r (0..63), 16-byte chunk c (columns 8 c .. 8 c + 7 of the block).
 __device__ __forceinline__ u32x4_t staged_chunk(const lds_u8_t* stg, int r, int c) {
   return *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>(
-      stg + r * 128 + (c ^ ((r >> 1) & 7)) * 16);
+      stg + r * 256 + (c ^ (r & 15)) * 16);
 }
 
 // The block stored as bf16 (columns at or past `split` go to C1 at column
 // n - split; rows >= m_end and columns >= n_end are not stored).
-__device__ __forceinline__ void store_block(const f32x16_t acc[2][2], lds_u8_t* stg, int m0,
+__device__ __forceinline__ void store_block(const f32x16_t acc[2][4], lds_u8_t* stg, int m0,
                                             int m_end, int n0, int n_end, int split,
                                             uint16_t* C0, uint16_t* C1, int64_t ldc, int lane) {
   stage_block(acc, stg, lane);
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const int r = 8 * t + lane / 8, c = lane % 8;
+  for (int t = 0; t < 16; ++t) {
+    const int r = 4 * t + lane / 16, c = lane % 16;
     const u32x4_t v = staged_chunk(stg, r, c);
     const int m = m0 + r, n = n0 + 8 * c;
     if (m < m_end && n < n_end) {
@@ -170,7 +174,7 @@ k_bgemm_sched(const int32_t* __restrict__ offsets, int E, int64_t N_cap, int32_t
 // rows and a ring of kKgStages direct-to-LDS stages (16 KB each), so that three
 // workgroups fit a CU: the tiles of small experts are short and latency-bound,
 // and more of them in flight is what they need.
-__global__ void __launch_bounds__(kThreads, 3)
+__global__ void __launch_bounds__(kThreads, 2)
 k_bgemm_kgroup(const uint16_t* __restrict__ A, int64_t lda, int M, const uint16_t* __restrict__ B,
                int64_t ldb, int N, const int32_t* __restrict__ ws, int E,
                const uint16_t* __restrict__ zeros, uint16_t* __restrict__ C0,
@@ -203,15 +207,22 @@ k_bgemm_kgroup(const uint16_t* __restrict__ A, int64_t lda, int M, const uint16_
   const int wm = wave & 1, wn = wave >> 1;
 
   // Direct-to-LDS loads: load l fills slot c = l * 256 + wave * 64 + lane of
-  // each [k][col] operand tile, i.e. k row c / 16 and swizzled chunk c % 16,
-  // so the lane loads global column chunk (c % 16) ^ 4 (k & 3).
-  int krow[kKgLoads], colA[kKgLoads], colB[kKgLoads];
+  // each [k][col] operand tile, i.e. k row c / (W / 8) and swizzled chunk
+  // c % (W / 8) for a tile W columns wide (A: 128, B: 256), so the lane loads
+  // global column chunk (c % (W / 8)) ^ 4 (k & 3).
+  int krowA[kKgLoadsA], colA[kKgLoadsA], krowB[kKgLoadsB], colB[kKgLoadsB];
 #pragma unroll
-  for (int l = 0; l < kKgLoads; ++l) {
+  for (int l = 0; l < kKgLoadsA; ++l) {
     const int c = l * kThreads + wave * kWave + lane;
-    krow[l] = c >> 4;
-    const int cc = (c & 15) ^ (4 * (krow[l] & 3));
+    krowA[l] = c >> 4;
+    const int cc = (c & 15) ^ (4 * (krowA[l] & 3));
     colA[l] = std::min(m0 + cc * 8, M - 8);
+  }
+#pragma unroll
+  for (int l = 0; l < kKgLoadsB; ++l) {
+    const int c = l * kThreads + wave * kWave + lane;
+    krowB[l] = c >> 5;
+    const int cc = (c & 31) ^ (4 * (krowB[l] & 3));
     colB[l] = std::min(n0 + cc * 8, N - 8);
   }
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
@@ -222,29 +233,29 @@ k_bgemm_kgroup(const uint16_t* __restrict__ A, int64_t lda, int M, const uint16_
                                                  wave * kWave * 16));
     const int r0 = r_lo + issued * kKgTK;
 #pragma unroll
-    for (int l = 0; l < kKgLoads; ++l) {
-      const int r = r0 + krow[l];
+    for (int l = 0; l < kKgLoadsA; ++l) {
+      const int r = r0 + krowA[l];
       const bool in = r < r_hi;
       load_lds16(in ? A + int64_t(r) * lda + colA[l] : zeros, st + l * kThreads * 16);
     }
 #pragma unroll
-    for (int l = 0; l < kKgLoads; ++l) {
-      const int r = r0 + krow[l];
+    for (int l = 0; l < kKgLoadsB; ++l) {
+      const int r = r0 + krowB[l];
       const bool in = r < r_hi;
-      load_lds16(in ? B + int64_t(r) * ldb + colB[l] : zeros, st + kKgTile + l * kThreads * 16);
+      load_lds16(in ? B + int64_t(r) * ldb + colB[l] : zeros, st + kKgTileA + l * kThreads * 16);
     }
     ++issued;
   };
-  int offA[2][2], offB[2][2];
+  int offA[2][2], offB[4][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) tr_offsets(wm * 64 + 32 * i, lane, offA[i]);
+  for (int i = 0; i < 2; ++i) tr_offsets<TM>(wm * 64 + 32 * i, lane, offA[i]);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) tr_offsets(wn * 64 + 32 * j, lane, offB[j]);
-  f32x16_t acc[2][2];
+  for (int j = 0; j < 4; ++j) tr_offsets<TN>(wn * 128 + 32 * j, lane, offB[j]);
+  f32x16_t acc[2][4];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   // Stage i goes to buffer i % kKgStages, kKgStages - 1 stages ahead of the
@@ -252,7 +263,7 @@ k_bgemm_kgroup(const uint16_t* __restrict__ A, int64_t lda, int M, const uint16_
   while (issued < kKgStages - 1 && issued < ksteps) issue();
   for (int ks = 0; ks < ksteps; ++ks) {
     static_assert(kKgStages == 3, "one later stage at most is in flight at a wait");
-    if (issued - ks - 1 >= 1) wait_vmcnt<2 * kKgLoads>();
+    if (issued - ks - 1 >= 1) wait_vmcnt<kKgLoadsA + kKgLoadsB>();
     else wait_vmcnt<0>();
     // every wave's part of stage ks is in LDS, and every wave is done reading
     // stage ks - 1 (its MFMAs consumed those reads), whose buffer the issue
@@ -260,18 +271,18 @@ k_bgemm_kgroup(const uint16_t* __restrict__ A, int64_t lda, int M, const uint16_
     stage_barrier();
     if (issued < ksteps) issue();
     const lds_u8_t* ta = lds + (ks % kKgStages) * kKgStage;
-    const lds_u8_t* tb = ta + kKgTile;
+    const lds_u8_t* tb = ta + kKgTileA;
 #pragma unroll
     for (int kk = 0; kk < kKgTK / 16; ++kk) {
-      bf16x8_t fa[2], fb[2];
+      bf16x8_t fa[2], fb[4];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) fa[i] = read_kc(ta, offA[i], kk);
+      for (int i = 0; i < 2; ++i) fa[i] = read_kc<TM>(ta, offA[i], kk);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) fb[j] = read_kc(tb, offB[j], kk);
+      for (int j = 0; j < 4; ++j) fb[j] = read_kc<TN>(tb, offB[j], kk);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 4; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0);
     }
   }
@@ -281,7 +292,8 @@ k_bgemm_kgroup(const uint16_t* __restrict__ A, int64_t lda, int M, const uint16_
   const int64_t ebase = int64_t(e) * M * ldc;
   // the LDS is free: every wave has passed the k-loop's last barrier (or, for
   // an expert without rows, never used it)
-  store_block(acc, lds + wave * 8192, m0 + wm * 64, M, n0 + wn * 64, N, split, C0 + ebase,
+  static_assert(4 * 16384 <= kKgStages * kKgStage, "the staging areas fit the ring");
+  store_block(acc, lds + wave * 16384, m0 + wm * 64, M, n0 + wn * 128, N, split, C0 + ebase,
               C1 + ebase, ldc, lane);
 }
 

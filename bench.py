@@ -8,8 +8,8 @@ resident in HBM before timing starts. `value` is tokens/s of that step.
 
 The same run also times every call at the other workloads (permute/combine
 at T=4096 H=2048 E=64 K=6; reorder + special-expert combine of the R=8 x 32
-receive buffer; the unpermute backward at T=16384 H=4096), each with a 1 GiB
-cache flush before every timed launch, and the CPU oracle on a bounded sample
+receive buffer; the unpermute backward at T=16384 H=4096), each after a 1 GiB
+read that flushes the caches before every timed launch, and the CPU oracle on a bounded sample
 of the layer workload (`cpu_baseline`). One JSON line goes to stdout.
 
     python bench.py [--steps K] [--warmup W] [--no-ops] [--no-cpu-baseline]
@@ -68,15 +68,20 @@ def dt(a, dev):
 
 
 class Flusher:
-    """Writes 1 GiB between timed launches so no input sits in the 256 MB
-    Infinity Cache or the L2s when a timed launch starts."""
+    """Reads 1 GiB between timed launches, so no input sits in the 256 MB
+    Infinity Cache or the L2s when a timed launch starts and no dirty line is
+    left there either: a flush that writes (a 1 GiB fill) leaves up to the
+    caches' size in dirty lines, whose write-back to HBM then lands inside the
+    next timed launch and is charged to it."""
 
     def __init__(self, dev):
         import torch
-        self.buf = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        self.buf = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        self.sink = torch.empty((), dtype=torch.float32, device=dev)
 
     def __call__(self):
-        self.buf.fill_(1.0)
+        import torch
+        torch.sum(self.buf, dim=0, out=self.sink)
 
 
 def time_op(fn, iters, flush=None, warm=2):
@@ -625,7 +630,7 @@ def main():
     for name, fn, col, nbytes in mem_ops:
         if flush is not None:
             us, usmin = time_op(fn, args.op_iters, flush)
-            timing = "alone, cache flushed"
+            timing = "alone, caches flushed by a 1 GiB read"
         elif col is None:
             continue
         else:

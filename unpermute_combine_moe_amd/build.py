@@ -55,7 +55,27 @@ def build(verbose: bool = False) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    build_probes(verbose)
     return LIB
+
+
+def build_probes(verbose: bool = False) -> list:
+    """Compile the measurement aids under probes/ (stand-alone executables,
+    not part of the library) into _build/probes/, so that they keep building."""
+    out_dir = os.path.join(ROOT, "_build", "probes")
+    os.makedirs(out_dir, exist_ok=True)
+    outs = []
+    for src in sorted(glob.glob(os.path.join(PKG, "probes", "*.hip"))):
+        exe = os.path.join(out_dir, os.path.splitext(os.path.basename(src))[0])
+        cmd = [HIPCC, "-std=c++17", "-O3", f"--offload-arch={ARCH}", "-Xclang", "-target-feature",
+               "-Xclang", "-packed-fp32-ops", src, "-o", exe]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{r.stdout}{r.stderr}")
+        outs.append(exe)
+    return outs
 
 
 if __name__ == "__main__":

@@ -241,6 +241,144 @@ k_step(int nsteps, const uint16_t* __restrict__ src, float* __restrict__ out,
   }
 }
 
+// The same work per k-step (4.19 MFLOP per workgroup) as a 256 x 256 tile
+// with BK = 32: four waves of 128 x 128 (four A and four B fragments each,
+// 256 accumulator registers), a four-stage ring of 32 KB (A rows of 64 bytes,
+// B rows of 512 bytes), the loads of stage s + 3 issued during step s. Per
+// k-step LDS carries 32 KB of loads and 64 KB of fragment reads instead of 48
+// and 96.
+constexpr int kStage2 = 32 * 1024;
+constexpr int kStages2 = 4;
+__device__ __forceinline__ int swz2(int row, int kc) { return row * 4 + (kc ^ ((row >> 1) & 3)); }
+
+template <int kF>
+__global__ void __launch_bounds__(kThreads, 1)
+k_step_256(int nsteps, const uint16_t* __restrict__ src, float* __restrict__ out,
+           unsigned long long* __restrict__ clk) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  lds_u8_t* lds = (lds_u8_t*)(smem);
+  constexpr bool mfma = kF & kMfma, reads = kF & kReads, loads = kF & kLdsLoads;
+  for (int i = threadIdx.x; i < kStages2 * kStage2 / 2; i += kThreads)
+    reinterpret_cast<__attribute__((address_space(3))) uint16_t*>(lds)[i] = random_bf16(i);
+  __syncthreads();
+  const int lane = threadIdx.x % 64, wave = threadIdx.x / 64;
+  const int wm = wave & 1, wn = wave >> 1;
+  constexpr int kAOff = 0, kBOff = 16 * 1024;
+  int b_off[4][2];
+  {
+    const int g16 = lane / 16, i16 = lane % 16;
+    for (int j = 0; j < 4; ++j) {
+      const int n = wn * 128 + j * 32 + 16 * (g16 % 2) + 4 * (i16 % 4);
+      for (int half = 0; half < 2; ++half) {
+        const int k = 8 * (g16 / 2) + i16 / 4 + 4 * half;
+        b_off[j][half] = kBOff + swz_b(k, n / 8) * 16 + (n % 8) * 2;
+      }
+    }
+  }
+  // read r (0..11) of sub-step kk: A fragments 0..3, then the halves of B fragments 0..3
+  auto rd = [&](const lds_u8_t* st, int kk, int r, bf16x8_t* na, bf16x8_t* nb) {
+    if (r < 4) {
+      na[r] = read16(st + kAOff, swz2(wm * 128 + r * 32 + lane % 32, kk * 2 + lane / 32));
+      return;
+    }
+    const int jj = (r - 4) / 2, half = (r - 4) % 2;
+    const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_v4i16_t*)(st + b_off[jj][half] + kk * 16 * (BN * 2)));
+    __builtin_memcpy(reinterpret_cast<char*>(&nb[jj]) + 8 * half, &v, 8);
+  };
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lds));
+  auto load_lds = [&](int stage, int i, int s) {  // i = 0..7
+    const uint16_t* g = src + (s & 1) * kSrcElems + (i * kThreads + wave * 64 + lane) * 8;
+    const uint32_t m = lds0 + stage * kStage2 + (i * kThreads + wave * 64) * 16;
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(g), "s"(__builtin_amdgcn_readfirstlane(m))
+                 : "memory", "m0");
+  };
+  if (loads) {
+    for (int st = 0; st < 3; ++st)
+      for (int i = 0; i < 8; ++i) load_lds(st, i, st);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+  __syncthreads();
+  f32x16_t acc[4][4];
+  for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 4; ++j)
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  bf16x8_t fa[2][4], fb[2][4];
+  for (int r = 0; r < 12; ++r) {
+    rd(lds, 0, r, fa[0], fb[0]);
+    rd(lds, 1, r, fa[1], fb[1]);
+  }
+  uint32_t xsum = 0;
+  auto mm = [&](int c, int i, int jj) {
+    if (mfma) {
+      acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[c][jj], fa[c][i], acc[i][jj], 0, 0, 0);
+    } else {
+      u32x4_t a, b;
+      __builtin_memcpy(&a, &fa[c][i], 16);
+      __builtin_memcpy(&b, &fb[c][jj], 16);
+      xsum += a.x + a.y + a.z + a.w + b.x + b.y + b.z + b.w;
+    }
+  };
+  wait_lds();
+  const unsigned long long t0 = __builtin_readcyclecounter();
+  const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
+  asm volatile("" ::"s"(t0), "s"(r0));
+  int cbuf = 0;
+  for (int s = 0; s < nsteps; ++s) {
+    const lds_u8_t* st = lds + cbuf * kStage2;
+    const int refill = cbuf == 0 ? kStages2 - 1 : cbuf - 1;  // stage s + 3 = stage s - 1's buffer
+    cbuf = cbuf + 1 == kStages2 ? 0 : cbuf + 1;
+    // sub-step 0: the reads of sub-step 1 after MFMAs 0..5, the loads after MFMAs 6..13
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      mm(0, m / 4, m % 4);
+      __builtin_amdgcn_sched_barrier(0);
+      if (reads && m < 6) {
+        rd(st, 1, 2 * m, fa[1], fb[1]);
+        rd(st, 1, 2 * m + 1, fa[1], fb[1]);
+      } else if (loads && m >= 6 && m < 14) {
+        load_lds(refill, m - 6, s);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // sub-step 1: two MFMAs, the hand-over, then the next stage's first reads
+    mm(1, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mm(1, 0, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (loads) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    wait_lds();
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    const lds_u8_t* nst = lds + cbuf * kStage2;
+#pragma unroll
+    for (int m = 2; m < 16; ++m) {
+      mm(1, m / 4, m % 4);
+      __builtin_amdgcn_sched_barrier(0);
+      if (reads && m < 8) {
+        rd(nst, 0, 2 * (m - 2), fa[0], fb[0]);
+        rd(nst, 0, 2 * (m - 2) + 1, fa[0], fb[0]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  const unsigned long long t1 = __builtin_readcyclecounter();
+  const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
+  float sum = static_cast<float>(xsum);
+  for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 4; ++j)
+      for (int r = 0; r < 16; ++r) sum += acc[i][j][r];
+  out[blockIdx.x * kThreads + threadIdx.x] = sum;
+  if (threadIdx.x == 0) {
+    clk[2 * blockIdx.x] = t1 - t0;
+    clk[2 * blockIdx.x + 1] = r1 - r0;
+  }
+}
+
 void check(hipError_t e, const char* what) {
   if (e != hipSuccess) {
     std::fprintf(stderr, "%s: %s\n", what, hipGetErrorString(e));
@@ -260,6 +398,42 @@ void run(const char* name, int grid, int nsteps, const uint16_t* src, float* out
     check(hipEventCreate(&b), "hipEventCreate");
     check(hipEventRecord(a), "hipEventRecord");
     hipLaunchKernelGGL(k_step<kF>, dim3(grid), dim3(kThreads), kStages * kStageBytes, 0, nsteps,
+                       src, out, clk);
+    check(hipGetLastError(), "launch");
+    check(hipEventRecord(b), "hipEventRecord");
+    check(hipEventSynchronize(b), "hipEventSynchronize");
+    float ms = 0.f;
+    check(hipEventElapsedTime(&ms, a, b), "hipEventElapsedTime");
+    std::vector<unsigned long long> c(2 * grid);
+    check(hipMemcpy(c.data(), clk, c.size() * sizeof(c[0]), hipMemcpyDeviceToHost), "hipMemcpy");
+    double cy = 0, rt = 0;
+    for (int i = 0; i < grid; ++i) {
+      cy += c[2 * i];
+      rt += c[2 * i + 1];
+    }
+    cy /= grid;
+    rt /= grid;
+    std::printf("%-58s %6.3f ms  %7.1f cycles/k-step  %.2f GHz  %5.0f ns/k-step\n", name, ms,
+                cy / nsteps, cy / rt * 0.1, rt * 10.0 / nsteps);
+    std::fflush(stdout);
+    check(hipEventDestroy(a), "hipEventDestroy");
+    check(hipEventDestroy(b), "hipEventDestroy");
+  }
+}
+
+
+template <int kF>
+void run256(const char* name, int grid, int nsteps, const uint16_t* src, float* out,
+            unsigned long long* clk) {
+  check(hipFuncSetAttribute(reinterpret_cast<const void*>(k_step_256<kF>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kStages2 * kStage2),
+        "hipFuncSetAttribute");
+  for (int rep = 0; rep < 2; ++rep) {
+    hipEvent_t a, b;
+    check(hipEventCreate(&a), "hipEventCreate");
+    check(hipEventCreate(&b), "hipEventCreate");
+    check(hipEventRecord(a), "hipEventRecord");
+    hipLaunchKernelGGL(k_step_256<kF>, dim3(grid), dim3(kThreads), kStages2 * kStage2, 0, nsteps,
                        src, out, clk);
     check(hipGetLastError(), "launch");
     check(hipEventRecord(b), "hipEventRecord");
@@ -312,5 +486,8 @@ int main() {
   run<kFull | kBNMajor>("MFMAs + reads + barrier, B n-major (b128 reads)", grid, nsteps, src, out, clk);
   run<kFull | kLdsLoads | kBNMajor>("whole k-step, direct-to-LDS loads, B n-major", grid, nsteps, src, out, clk);
   run<kFull | kRegLoads>("whole k-step, loads into registers + ds_write_b128", grid, nsteps, src, out, clk);
+  run256<kMfma | kReads>("256 x 256 tile, BK 32: MFMAs + fragment reads + barrier", grid, nsteps, src, out, clk);
+  run256<kReads | kLdsLoads>("256 x 256 tile, BK 32: fragment reads + direct-to-LDS loads", grid, nsteps, src, out, clk);
+  run256<kMfma | kReads | kLdsLoads>("256 x 256 tile, BK 32: whole k-step", grid, nsteps, src, out, clk);
   return 0;
 }

@@ -508,10 +508,14 @@ def run_ops(args, dev, flush):
     # device-to-device copy of 1 GiB for reference
     a = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev)
     b = torch.empty_like(a)
-    us, usmin = time_op(lambda: b.copy_(a), 10, None)
+    us, usmin = time_op(lambda: b.copy_(a), 10, flush)
     ops.append(dict(workload="d2d_copy_1GiB", **op_entry("torch_copy", us, usmin,
                                                          nbytes=2 * a.numel() * 2)))
     del a, b
+    # every memory-bound entry above was timed alone, each launch after the flush
+    for e in ops:
+        if "hbm_frac" in e and flush is not None:
+            e.setdefault("timing", "alone, caches flushed by a 1 GiB read")
     # for scale: the vendor GEMM (torch.matmul, hipBLASLt) on dense bf16 matrices
     # of the skewed layer's two passes, all 65,536 rows as one matrix (no expert
     # groups, no SwiGLU), weights [k][n] as the grouped call takes them

@@ -6,7 +6,7 @@
 // slot s = t*K + k with a real id lands at
 //     expert_offsets[id] + #{ s' < s : id(s') == id }.
 //
-// Layout of the work: the T*K slots are cut into chunks of kChunkWaves waves x
+// Layout of the work: the T*K slots are cut into chunks of 4 (or 16) waves x
 // 64 lanes x `iters` slots; wave w of a chunk owns a contiguous run of
 // 64*iters slots, so "earlier wave" means "earlier slots". Three launches:
 //  1. per chunk: its (chunk, expert) count table row and every slot's rank
@@ -26,10 +26,12 @@ namespace {
 
 constexpr int kChunkWaves = 4;
 constexpr int kChunkThreads = kChunkWaves * kWave;
+constexpr int kChunkWavesWide = 16;  // chunks of a table the row kernel scans itself
 constexpr int kMaxExpertsPermute = 1024;
 constexpr int kMaxTopK = 16;
 
 struct PermutePlan {
+  int waves;    // waves per chunk (one workgroup of the rank kernel)
   int iters;    // slots per lane per chunk
   int64_t chunk;
   int64_t nblk; // number of chunks
@@ -38,14 +40,30 @@ struct PermutePlan {
 // Chunks are sized so the (chunk, expert) count table holds at most
 // kTableMax entries (one workgroup scans it), with at least two slots per lane.
 constexpr int64_t kTableMax = 16384;
+// Tables of at most kFusedTable entries are scanned by every row workgroup
+// itself (no scan launch).
+constexpr int kFusedTable = 4096;
 
-PermutePlan plan_for(int64_t S, int E) {
+PermutePlan plan_with(int64_t S, int E, int waves, int64_t table_max) {
   PermutePlan p;
-  const int64_t target = std::max<int64_t>(1, std::min<int64_t>(256, kTableMax / E));
-  p.iters = static_cast<int>(std::max<int64_t>(2, ceil_div(S, int64_t(kChunkThreads) * target)));
-  p.chunk = int64_t(kChunkThreads) * p.iters;
+  p.waves = waves;
+  const int64_t threads = int64_t(waves) * kWave;
+  const int64_t target = std::max<int64_t>(1, std::min<int64_t>(256, table_max / E));
+  p.iters = static_cast<int>(std::max<int64_t>(2, ceil_div(S, threads * target)));
+  p.chunk = threads * p.iters;
   p.nblk = ceil_div(S, p.chunk);
   return p;
+}
+
+// Four waves per chunk; when that table is too big for the row kernel's own
+// scan, chunks of sixteen waves instead if their table fits it (at E >= 64
+// the same slots per lane, so as many waves rank them; E <= 512 keeps the rank
+// kernel's per-wave counts within 32 KB of LDS).
+PermutePlan plan_for(int64_t S, int E) {
+  const PermutePlan p = plan_with(S, E, kChunkWaves, kTableMax);
+  if (p.nblk * E <= kFusedTable || E > 512) return p;
+  const PermutePlan q = plan_with(S, E, kChunkWavesWide, kFusedTable);
+  return q.nblk * E <= kFusedTable ? q : p;
 }
 
 // Lanes of this wave holding the same key (key < 2^nbits).
@@ -70,16 +88,18 @@ constexpr int kBatch = 8;
 // slots; lanes holding the same id are found with a ballot per id bit (a
 // wave-level match), ranked with mbcnt, and the group's lowest lane advances
 // the wave's running count in LDS -- deterministic, no global atomics.
-__global__ void __launch_bounds__(kChunkThreads)
+template <int kW>
+__global__ void __launch_bounds__(kW * kWave)
 k_route_rank(const int32_t* __restrict__ ids, SlotMask mk, int64_t S, int E, int iters,
              int32_t* __restrict__ table, int32_t* __restrict__ row_of_slot) {
-  extern __shared__ int32_t run[];  // [kChunkWaves * E]
+  constexpr int kThreads = kW * kWave;
+  extern __shared__ int32_t run[];  // [kW * E]
   const int w = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
   const int64_t b = blockIdx.x;
-  for (int i = threadIdx.x; i < kChunkWaves * E; i += kChunkThreads) run[i] = 0;
+  for (int i = threadIdx.x; i < kW * E; i += kThreads) run[i] = 0;
   __syncthreads();
-  const int64_t wbase = b * int64_t(kChunkThreads) * iters + int64_t(w) * kWave * iters;
+  const int64_t wbase = b * int64_t(kThreads) * iters + int64_t(w) * kWave * iters;
   int32_t* my = run + w * E;
   // ids of slots wbase + (j0 + q) * 64 + lane, q < kBatch
   // (slots outside the active mask read as id -1)
@@ -112,10 +132,10 @@ k_route_rank(const int32_t* __restrict__ ids, SlotMask mk, int64_t S, int E, int
   __syncthreads();
   // the chunk's histogram, and the first rank of every (wave, expert) inside
   // the chunk: the counts of the earlier waves
-  for (int e = threadIdx.x; e < E; e += kChunkThreads) {
+  for (int e = threadIdx.x; e < E; e += kThreads) {
     int32_t r = 0;
 #pragma unroll
-    for (int ww = 0; ww < kChunkWaves; ++ww) {
+    for (int ww = 0; ww < kW; ++ww) {
       const int32_t c = run[ww * E + e];
       run[ww * E + e] = r;
       r += c;
@@ -254,7 +274,6 @@ k_route_empty(int E, int32_t* __restrict__ counts, int32_t* __restrict__ offsets
 // counts and offsets.
 constexpr int kRowWaves = 4;
 constexpr int kRowBatch = 4;  // 16-byte chunks per lane loaded before their stores
-constexpr int kFusedTable = 4096;
 constexpr int kTableLoads = kFusedTable / (kRowWaves * kWave);  // per thread
 template <bool kScanHere>
 __global__ void __launch_bounds__(kRowWaves * kWave)
@@ -460,9 +479,14 @@ hipError_t launch_permute(const uint16_t* x, const int32_t* ids, SlotMask mk, in
     hipLaunchKernelGGL(k_route_empty, dim3(1), dim3(kChunkThreads), 0, st, E, counts, offsets);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(k_route_rank, dim3(static_cast<unsigned>(p.nblk)), dim3(kChunkThreads),
-                     size_t(kChunkWaves) * E * sizeof(int32_t), st, ids, mk, S, E, p.iters, table,
-                     row_of_slot);
+  if (p.waves == kChunkWavesWide)
+    hipLaunchKernelGGL(k_route_rank<kChunkWavesWide>, dim3(static_cast<unsigned>(p.nblk)),
+                       dim3(kChunkWavesWide * kWave), size_t(kChunkWavesWide) * E * sizeof(int32_t),
+                       st, ids, mk, S, E, p.iters, table, row_of_slot);
+  else
+    hipLaunchKernelGGL(k_route_rank<kChunkWaves>, dim3(static_cast<unsigned>(p.nblk)),
+                       dim3(kChunkThreads), size_t(kChunkWaves) * E * sizeof(int32_t), st, ids, mk,
+                       S, E, p.iters, table, row_of_slot);
   // two waves per token when there are too few tokens for several rounds of waves
   const int nsplit = (permuted != nullptr && H / 8 >= 2 * kWave && T < kSplitBelowTokens) ? 2 : 1;
   const dim3 grid(static_cast<unsigned>(ceil_div(T, kRowWaves / nsplit)));

@@ -607,7 +607,7 @@ def main():
     g_tf = gemm_flops(n_rows, H, I) / (g_us * 1e-6) / 1e12
     active = int((d["counts"] > 0).sum().item())
     rec = gemm_traffic_record()
-    roofline = {"bound": "mfma", "kernel": "moe_grouped_gemm_swiglu (sched + gate/up + down)",
+    roofline = {"bound": "mfma", "kernel": "moe_grouped_gemm_swiglu (gate/up + down)",
                 "achieved": round(g_tf, 1), "peak": BF16_DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(g_tf / BF16_DENSE_PEAK_TFLOPS, 4),
                 "traffic": rec["traffic_bytes"] if rec else None,

@@ -68,7 +68,6 @@ constexpr int BN = 256;  // B-columns per tile
 constexpr int BK = 64;
 constexpr int kChunksA = BM * BK / 8;  // 16-byte chunks per stage
 constexpr int kChunksB = BN * BK / 8;
-constexpr int kSchedThreads = 1024;
 constexpr int kMaxExperts = 1024;
 constexpr int kXcds = 8;
 
@@ -76,39 +75,6 @@ constexpr int kXcds = 8;
 // over all 16 bank groups of 16 bytes)
 __device__ __forceinline__ int swz(int row, int kc) { return row * (BK / 8) + (kc ^ ((row >> 1) & 7)); }
 
-// ws layout (int32): tile_prefix[E+1] | offs[E+1]
-__global__ void __launch_bounds__(kSchedThreads)
-k_gemm_sched(const int32_t* __restrict__ offsets, int E, int64_t N_cap, int32_t* __restrict__ ws) {
-  __shared__ int32_t part[kSchedThreads];
-  int32_t* prefix = ws;
-  int32_t* offs = ws + (E + 1);
-  // clamped, non-decreasing offsets (a caller contract violation cannot push
-  // a row index outside [0, N_cap])
-  const int e = threadIdx.x;
-  int32_t lo = 0, hi = 0;
-  if (e < E) {
-    lo = static_cast<int32_t>(std::min<int64_t>(std::max(offsets[e], 0), N_cap));
-    hi = static_cast<int32_t>(std::min<int64_t>(std::max(offsets[e + 1], 0), N_cap));
-    hi = std::max(hi, lo);
-  }
-  const int32_t tiles = (e < E) ? (hi - lo + BM - 1) / BM : 0;
-  part[e] = tiles;
-  __syncthreads();
-  for (int off = 1; off < kSchedThreads; off <<= 1) {
-    const int32_t v = e >= off ? part[e - off] : 0;
-    __syncthreads();
-    part[e] += v;
-    __syncthreads();
-  }
-  if (e < E) {
-    prefix[e] = part[e] - tiles;
-    offs[e] = lo;
-    if (e == E - 1) {
-      prefix[E] = part[e];
-      offs[E] = hi;
-    }
-  }
-}
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
@@ -227,19 +193,57 @@ __device__ __forceinline__ void global_load_lds16_step(const uint16_t*& p, uint6
 template <int kMode>
 __global__ void __launch_bounds__(Layout<kMode>::kThreads, 1)
 k_gemm(const uint16_t* __restrict__ A, int Kdim, const uint16_t* __restrict__ B0,
-       const uint16_t* __restrict__ B1, int Ncols, const int32_t* __restrict__ ws, int E,
-       uint16_t* __restrict__ C, const uint16_t* __restrict__ aux, float* __restrict__ preact,
-       int ksplit) {
+       const uint16_t* __restrict__ B1, int Ncols, const int32_t* __restrict__ offsets, int E,
+       int64_t N_cap, uint16_t* __restrict__ C, const uint16_t* __restrict__ aux,
+       float* __restrict__ preact, int ksplit) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kStages * kStageBytes];
-  // row-tile prefix and clamped expert offsets, staged once per workgroup so the
-  // per-tile expert lookup is a binary search in LDS
+  // row-tile prefix and clamped expert offsets, built once per workgroup in LDS
+  // for the per-tile expert lookup
   __shared__ int32_t s_prefix[kMaxExperts + 1];
   __shared__ int32_t s_offs[kMaxExperts + 1];
   lds_u8_t* lds = (lds_u8_t*)(smem);
   using L = Layout<kMode>;
-  for (int i = threadIdx.x; i <= E; i += L::kThreads) {
-    s_prefix[i] = ws[i];
-    s_offs[i] = ws[E + 1 + i];
+  // Wave 0 builds them from the device offsets, clamped to [0, N_cap] (a
+  // caller contract violation cannot push a row index outside the buffers):
+  // lane l takes experts l * per .. l * per + per - 1 (per = ceil(E / 64) <= 16),
+  // expert e gets ceil((max(hi, lo) - lo) / BM) row tiles, and a prefix of the
+  // lane sums across the wave places them.
+  if (threadIdx.x < kWave) {
+    constexpr int kPer = kMaxExperts / kWave;
+    const int ln = threadIdx.x;
+    const int per = (E + kWave - 1) / kWave;
+    const int e0 = std::min(E, ln * per);
+    auto clamp_off = [&](int e) {
+      return static_cast<int32_t>(std::min<int64_t>(std::max<int64_t>(offsets[e], 0), N_cap));
+    };
+    int32_t c[kPer + 1];
+#pragma unroll
+    for (int q = 0; q <= kPer; ++q) c[q] = (q <= per && e0 + q <= E) ? clamp_off(e0 + q) : 0;
+    int32_t tiles[kPer];
+    int32_t sum = 0;
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      int32_t t = 0;
+      if (q < per && e0 + q < E) t = (std::max(c[q + 1], c[q]) - c[q] + BM - 1) / BM;
+      tiles[q] = t;
+      sum += t;
+    }
+    int32_t incl = sum;
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int32_t v = __shfl_up(incl, o, kWave);
+      if (ln >= o) incl += v;
+    }
+    int32_t run = incl - sum;
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      if (q < per && e0 + q < E) {
+        s_prefix[e0 + q] = run;
+        s_offs[e0 + q] = c[q];
+        run += tiles[q];
+      }
+    }
+    if (ln == kWave - 1) s_prefix[E] = incl;
+    if (ln == 0) s_offs[E] = std::max(clamp_off(E), clamp_off(E - 1));  // the last expert's end
   }
   __syncthreads();
   const int32_t* prefix = s_prefix;
@@ -744,7 +748,9 @@ int persistent_grid() {
   return std::max(kXcds, (cus / kXcds) * kXcds);
 }
 
-// ws layout: tile_prefix[E+1] | offs[E+1] (int32)
+// The forward builds its tile schedule in LDS and needs no workspace; the size
+// (the 2 (E + 1) int32 that a separate schedule launch once wrote) is kept, so a
+// workspace sized for it stays valid, and the backward's layout starts after it.
 size_t gemm_workspace_bytes(int E, int64_t /*N_cap*/, int /*H*/, int /*I*/) {
   return ((static_cast<size_t>(2 * (E + 1)) * 4 + 255) / 256) * 256;
 }
@@ -752,15 +758,13 @@ size_t gemm_workspace_bytes(int E, int64_t /*N_cap*/, int /*H*/, int /*I*/) {
 hipError_t launch_grouped_gemm_swiglu(const uint16_t* x, const int32_t* offsets, int E,
                                       int64_t N_cap, int H, int I, const uint16_t* wg,
                                       const uint16_t* wu, const uint16_t* wd, uint16_t* h,
-                                      uint16_t* y, float* preact, void* ws, hipStream_t st) {
-  int32_t* w = static_cast<int32_t*>(ws);
-  hipLaunchKernelGGL(k_gemm_sched, dim3(1), dim3(kSchedThreads), 0, st, offsets, E, N_cap, w);
+                                      uint16_t* y, float* preact, void* /*ws*/, hipStream_t st) {
   if (N_cap == 0) return hipGetLastError();
   const int G = persistent_grid();
-  hipLaunchKernelGGL(k_gemm<0>, dim3(G), dim3(Layout<0>::kThreads), 0, st, x, H, wg, wu, I, w, E,
-                     h, nullptr, preact, 0);
-  hipLaunchKernelGGL(k_gemm<1>, dim3(G), dim3(Layout<1>::kThreads), 0, st, h, I, wd, nullptr, H, w,
-                     E, y, nullptr, nullptr, 0);
+  hipLaunchKernelGGL(k_gemm<0>, dim3(G), dim3(Layout<0>::kThreads), 0, st, x, H, wg, wu, I,
+                     offsets, E, N_cap, h, nullptr, preact, 0);
+  hipLaunchKernelGGL(k_gemm<1>, dim3(G), dim3(Layout<1>::kThreads), 0, st, h, I, wd, nullptr, H,
+                     offsets, E, N_cap, y, nullptr, nullptr, 0);
   return hipGetLastError();
 }
 
@@ -803,13 +807,11 @@ hipError_t launch_grouped_gemm_swiglu_grad(const uint16_t* x, const int32_t* off
   size_t off_bt, off_zero, off_dh, off_dgu;
   gemm_grad_layout(E, N_cap, I, &off_bt, &off_zero, &off_dh, &off_dgu);
   char* base = static_cast<char*>(ws);
-  int32_t* w = static_cast<int32_t*>(ws);
   int32_t* bt = reinterpret_cast<int32_t*>(base + off_bt);
   uint16_t* zeros = reinterpret_cast<uint16_t*>(base + off_zero);
   uint16_t* dh = reinterpret_cast<uint16_t*>(base + off_dh);
   uint16_t* dgu = reinterpret_cast<uint16_t*>(base + off_dgu);
   hipLaunchKernelGGL(k_fill_zero, dim3(1), dim3(64), 0, st, reinterpret_cast<uint32_t*>(zeros), 64);
-  hipLaunchKernelGGL(k_gemm_sched, dim3(1), dim3(kSchedThreads), 0, st, offsets, E, N_cap, w);
   hipError_t err = launch_bgemm_sched(offsets, E, N_cap, bt, st);
   if (err != hipSuccess) return err;
   if (N_cap > 0) {
@@ -817,18 +819,18 @@ hipError_t launch_grouped_gemm_swiglu_grad(const uint16_t* x, const int32_t* off
     if (preact != nullptr) {
       // [dg | du] straight from the dh GEMM (dy Wd^T, B_e = Wd[e] stored [I][H])
       hipLaunchKernelGGL(k_gemm<4>, dim3(G), dim3(Layout<4>::kThreads), 0, st, dy, H, wd, wd, I,
-                         w, E, dgu, nullptr, const_cast<float*>(preact), H);
+                         offsets, E, N_cap, dgu, nullptr, const_cast<float*>(preact), H);
     } else {
       // dh = dy Wd^T (B_e = Wd[e] stored [I][H]), then [dg | du] from the
       // recomputed gate and up tiles
       hipLaunchKernelGGL(k_gemm<3>, dim3(G), dim3(Layout<3>::kThreads), 0, st, dy, H, wd, wd, I,
-                         w, E, dh, nullptr, nullptr, H);
-      hipLaunchKernelGGL(k_gemm<2>, dim3(G), dim3(Layout<2>::kThreads), 0, st, x, H, wg, wu, I, w,
-                         E, dgu, dh, nullptr, 0);
+                         offsets, E, N_cap, dh, nullptr, nullptr, H);
+      hipLaunchKernelGGL(k_gemm<2>, dim3(G), dim3(Layout<2>::kThreads), 0, st, x, H, wg, wu, I,
+                         offsets, E, N_cap, dgu, dh, nullptr, 0);
     }
     // dx = [dg | du] [Wg ; Wu]^T: B_e = Wg[e], Wu[e] stored [H][I], side by side along k
     hipLaunchKernelGGL(k_gemm<3>, dim3(G), dim3(Layout<3>::kThreads), 0, st, dgu, 2 * I, wg, wu, H,
-                       w, E, dx, nullptr, nullptr, I);
+                       offsets, E, N_cap, dx, nullptr, nullptr, I);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }

@@ -792,12 +792,6 @@ size_t gemm_grad_workspace_bytes(int E, int64_t N_cap, int /*H*/, int I) {
   return gemm_grad_layout(E, N_cap, I, &a, &b, &c, &d);
 }
 
-namespace {
-__global__ void k_fill_zero(uint32_t* p, int n) {
-  if (static_cast<int>(threadIdx.x) < n) p[threadIdx.x] = 0u;
-}
-}  // namespace
-
 hipError_t launch_grouped_gemm_swiglu_grad(const uint16_t* x, const int32_t* offsets, int E,
                                            int64_t N_cap, int H, int I, const uint16_t* wg,
                                            const uint16_t* wu, const uint16_t* wd,
@@ -811,8 +805,7 @@ hipError_t launch_grouped_gemm_swiglu_grad(const uint16_t* x, const int32_t* off
   uint16_t* zeros = reinterpret_cast<uint16_t*>(base + off_zero);
   uint16_t* dh = reinterpret_cast<uint16_t*>(base + off_dh);
   uint16_t* dgu = reinterpret_cast<uint16_t*>(base + off_dgu);
-  hipLaunchKernelGGL(k_fill_zero, dim3(1), dim3(64), 0, st, reinterpret_cast<uint32_t*>(zeros), 64);
-  hipError_t err = launch_bgemm_sched(offsets, E, N_cap, bt, st);
+  hipError_t err = launch_bgemm_sched(offsets, E, N_cap, bt, zeros, st);
   if (err != hipSuccess) return err;
   if (N_cap > 0) {
     const int G = persistent_grid();

@@ -129,9 +129,12 @@ __device__ __forceinline__ void store_block(const f32x16_t acc[2][4], lds_u8_t* 
 // ws layout (int32): prefix[E+1] | offs[E+1] | order[E]
 //   prefix: row-tile prefix (ceil(rows_e / TM) per expert), offs: clamped
 //   offsets, order: experts by row count, largest first (ties: lower id first).
+// Also clears the 256-byte zero row that the contraction's ragged tail reads.
 __global__ void __launch_bounds__(kSchedThreads)
-k_bgemm_sched(const int32_t* __restrict__ offsets, int E, int64_t N_cap, int32_t* __restrict__ ws) {
+k_bgemm_sched(const int32_t* __restrict__ offsets, int E, int64_t N_cap, int32_t* __restrict__ ws,
+              uint32_t* __restrict__ zeros) {
   __shared__ int32_t part[kSchedThreads];
+  if (threadIdx.x < 64) zeros[threadIdx.x] = 0u;
   __shared__ int32_t rows[kSchedThreads];
   int32_t* prefix = ws;
   int32_t* offs = ws + (E + 1);
@@ -304,8 +307,9 @@ size_t bgemm_sched_bytes(int E) {
 }
 
 hipError_t launch_bgemm_sched(const int32_t* offsets, int E, int64_t N_cap, int32_t* ws,
-                              hipStream_t st) {
-  hipLaunchKernelGGL(k_bgemm_sched, dim3(1), dim3(kSchedThreads), 0, st, offsets, E, N_cap, ws);
+                              uint16_t* zeros, hipStream_t st) {
+  hipLaunchKernelGGL(k_bgemm_sched, dim3(1), dim3(kSchedThreads), 0, st, offsets, E, N_cap, ws,
+                     reinterpret_cast<uint32_t*>(zeros));
   return hipGetLastError();
 }
 

@@ -95,8 +95,9 @@ hipError_t launch_dered_combine(const uint16_t* src, const float* coeff, const i
 // CUs of the current device rounded down to a multiple of 8 (one per XCD slot)
 int persistent_grid();
 size_t bgemm_sched_bytes(int E);
+// also clears the 256-byte zero row `zeros`
 hipError_t launch_bgemm_sched(const int32_t* offsets, int E, int64_t N_cap, int32_t* ws,
-                              hipStream_t st);
+                              uint16_t* zeros, hipStream_t st);
 hipError_t launch_bgemm_kgroup(const uint16_t* A, int64_t lda, int M, const uint16_t* B,
                                int64_t ldb, int N, const int32_t* ws, int E,
                                const uint16_t* zeros, uint16_t* C0, uint16_t* C1, int split,

@@ -12,8 +12,9 @@
 //
 // Index math: one workgroup scans the flattened count table (the first
 // gathered row of every (source, expert) block) and the selected blocks in
-// destination order; the index kernel then gives every output position its
-// block by binary search, as the reorder does.
+// destination order (for tables and block lists of at most 2,048 entries every
+// index workgroup runs those scans itself instead); the index kernel then
+// gives every output position its block by binary search, as the reorder does.
 // Whiteboard: the scatter-add is turned into a segmented gather by destination
 // row. Each row's sources are counted (integer atomics: the counts do not
 // depend on the order), an exclusive scan of the counts gives each row its
@@ -71,12 +72,53 @@ k_dered_setup(const int32_t* __restrict__ counts, int oep, int E, int expert_sta
   if (threadIdx.x == 0) *total_p = total;
 }
 
+// kFused (count tables and block lists of at most kDeredFused entries): no
+// setup launch; every workgroup runs the setup's two scans itself in LDS (an
+// 8 KB L2 read of the counts per workgroup instead of a launch), and workgroup
+// 0 writes the per-destination counts.
+constexpr int kDeredFused = 2048;
+template <bool kFused>
 __global__ void __launch_bounds__(kIndexThreads)
 k_dered_index(const int32_t* __restrict__ ws, int64_t F, int B, int64_t capacity,
-              int32_t* __restrict__ indices, int32_t* __restrict__ total_out) {
-  const int32_t* blk_start = ws + F;
-  const int32_t* blk_dst = blk_start + 2 * B;
-  const int64_t total = blk_dst[B];
+              int32_t* __restrict__ indices, int32_t* __restrict__ total_out,
+              const int32_t* __restrict__ counts, int oep, int E, int expert_start, int iep_el,
+              int32_t* __restrict__ counts_by_dest) {
+  __shared__ int32_t s_flat[kFused ? kDeredFused : 1];
+  __shared__ int32_t s_start[kFused ? kDeredFused : 1];
+  __shared__ int32_t s_cnt[kFused ? kDeredFused : 1];
+  __shared__ int32_t s_dst[kFused ? kDeredFused : 1];
+  __shared__ int32_t s_part[kFused ? kIndexThreads : 1];
+  const int32_t* blk_start;
+  const int32_t* blk_dst;
+  int64_t total;
+  if (kFused) {
+    // the setup's scans, as k_dered_setup runs them
+    for (int i = threadIdx.x; i < F; i += kIndexThreads) s_flat[i] = max(counts[i], 0);
+    __syncthreads();
+    block_exclusive_scan<kIndexThreads>(s_flat, s_flat, F, s_part);
+    for (int b = threadIdx.x; b < B; b += kIndexThreads) {
+      const int src = b % oep;
+      const int dl = b / oep;
+      const int64_t cell = int64_t(src) * E + expert_start + dl;
+      s_start[b] = s_flat[cell];
+      s_cnt[b] = max(counts[cell], 0);
+    }
+    __syncthreads();
+    total = block_exclusive_scan<kIndexThreads>(s_cnt, s_dst, B, s_part);
+    if (blockIdx.x == 0) {
+      for (int dl = threadIdx.x; dl < iep_el; dl += kIndexThreads) {
+        int32_t sum = 0;
+        for (int src = 0; src < oep; ++src) sum += s_cnt[dl * oep + src];
+        counts_by_dest[dl] = sum;
+      }
+    }
+    blk_start = s_start;
+    blk_dst = s_dst;
+  } else {
+    blk_start = ws + F;
+    blk_dst = blk_start + 2 * B;
+    total = blk_dst[B];
+  }
   const int64_t i = int64_t(blockIdx.x) * kIndexThreads + threadIdx.x;
   if (i == 0 && total_out != nullptr) *total_out = static_cast<int32_t>(total);
   if (i >= capacity) return;
@@ -398,12 +440,19 @@ hipError_t launch_dered_indices(const int32_t* counts, int oep, int E, int exper
                                 int32_t* counts_by_dest, int32_t* total, void* ws,
                                 hipStream_t st) {
   int32_t* w = static_cast<int32_t*>(ws);
+  const int64_t F = int64_t(oep) * E;
+  const int B = iep * El * oep;
+  const int64_t n = capacity > 0 ? capacity : 1;  // one thread at least, for *total
+  const dim3 grid(static_cast<unsigned>(ceil_div(n, kIndexThreads)));
+  if (F <= kDeredFused && B <= kDeredFused) {
+    hipLaunchKernelGGL(k_dered_index<true>, grid, dim3(kIndexThreads), 0, st, w, F, B, capacity,
+                       indices, total, counts, oep, E, expert_start, iep * El, counts_by_dest);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(k_dered_setup, dim3(1), dim3(kSetupThreads), 0, st, counts, oep, E,
                      expert_start, iep, El, w, counts_by_dest);
-  const int64_t n = capacity > 0 ? capacity : 1;  // one thread at least, for *total
-  hipLaunchKernelGGL(k_dered_index, dim3(static_cast<unsigned>(ceil_div(n, kIndexThreads))),
-                     dim3(kIndexThreads), 0, st, w, int64_t(oep) * E, iep * El * oep, capacity,
-                     indices, total);
+  hipLaunchKernelGGL(k_dered_index<false>, grid, dim3(kIndexThreads), 0, st, w, F, B, capacity,
+                     indices, total, counts, oep, E, expert_start, iep * El, counts_by_dest);
   return hipGetLastError();
 }
 

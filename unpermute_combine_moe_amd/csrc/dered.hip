@@ -19,7 +19,7 @@
 // row. Each row's sources are counted (integer atomics: the counts do not
 // depend on the order), an exclusive scan of the counts gives each row its
 // segment of a source list, and every source index is placed in its row's
-// segment (the scan is one workgroup up to 16,384 rows, three kernels beyond).
+// segment (the scan is one workgroup up to 16,384 rows, two kernels beyond).
 // One wave per whiteboard row then writes the row once: zeros for no
 // source, the correctly rounded scaled row for one source (the common case:
 // the dispatch indices name distinct rows), and for several sources their
@@ -178,18 +178,23 @@ k_wb_block_sums(const int32_t* __restrict__ cnt, int64_t G, int32_t* __restrict_
   if (threadIdx.x == 0) bsum[blockIdx.x] = part[0];
 }
 
-// Exclusive scan of the block sums in place (one workgroup).
-__global__ void __launch_bounds__(1024) k_wb_scan_sums(int32_t* __restrict__ bsum, int64_t nb) {
-  __shared__ int32_t part[1024];
-  block_exclusive_scan<1024>(bsum, bsum, nb, part);
-}
-
 // start[r] = exclusive prefix of cnt; start[G] = number of placed sources.
-// cnt is cleared again, to count the placements.
+// cnt is cleared again, to count the placements. Each workgroup first adds up
+// the sums of the blocks before its own (a few loads: G / 4096 blocks).
 __global__ void __launch_bounds__(kScanThreads)
 k_wb_block_scan(int32_t* __restrict__ cnt, int64_t G, const int32_t* __restrict__ bsum,
                 int32_t* __restrict__ start) {
   __shared__ int32_t part[kScanThreads];
+  int32_t earlier = 0;
+  for (int64_t j = threadIdx.x; j < int64_t(blockIdx.x); j += kScanThreads) earlier += bsum[j];
+  part[threadIdx.x] = earlier;
+  __syncthreads();
+  for (int o = kScanThreads / 2; o > 0; o >>= 1) {
+    if (static_cast<int>(threadIdx.x) < o) part[threadIdx.x] += part[threadIdx.x + o];
+    __syncthreads();
+  }
+  const int32_t block_base = part[0];
+  __syncthreads();
   const int64_t base = int64_t(blockIdx.x) * kScanBlock + int64_t(threadIdx.x) * kScanPer;
   int32_t v[kScanPer];
   int32_t sum = 0;
@@ -206,7 +211,7 @@ k_wb_block_scan(int32_t* __restrict__ cnt, int64_t G, const int32_t* __restrict_
     part[threadIdx.x] += x;
     __syncthreads();
   }
-  int32_t run = bsum[blockIdx.x] + part[threadIdx.x] - sum;
+  int32_t run = block_base + part[threadIdx.x] - sum;
 #pragma unroll
   for (int i = 0; i < kScanPer; ++i) {
     if (base + i < G) {
@@ -227,8 +232,9 @@ k_wb_block_scan(int32_t* __restrict__ cnt, int64_t G, const int32_t* __restrict_
 constexpr int kOneWaves = 16;
 constexpr int kOneRows = 64;   // 64-element rows per wave
 constexpr int kOneBatch = 16;  // rows loaded together
-// Past 16,384 rows the three-launch scan over blocks of kScanBlock counts is
-// faster (at 65,536 rows: 125.6 against 141.2 us for the whole combine).
+// Past 16,384 rows the scan over blocks of kScanBlock counts (two launches) is
+// faster (at 65,536 rows: 125.6 against 141.2 us for the whole combine, when
+// it still took three launches).
 constexpr int64_t kOneScanMax = 16384;
 static_assert(kOneScanMax <= int64_t(kOneWaves) * kOneRows * kWave, "one workgroup's capacity");
 __global__ void __launch_bounds__(kOneWaves * kWave)
@@ -481,7 +487,6 @@ hipError_t launch_dered_combine(const uint16_t* src, const float* coeff, const i
   } else {
     hipLaunchKernelGGL(k_wb_block_sums, dim3(static_cast<unsigned>(nb)), dim3(kScanThreads), 0,
                        st, cnt, G, bsum);
-    hipLaunchKernelGGL(k_wb_scan_sums, dim3(1), dim3(1024), 0, st, bsum, nb);
     hipLaunchKernelGGL(k_wb_block_scan, dim3(static_cast<unsigned>(nb)), dim3(kScanThreads), 0,
                        st, cnt, G, bsum, start);
   }
